@@ -1,0 +1,311 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked here against what the pages and plain mathematics fix,
+never against itself: the byte table printed on the pages, hand-computed
+products, closed forms, exact extremes at the int32 bound, and numpy's int64
+matmul (a library routine) over a decode written separately from the page's
+byte table.  Each group below names the mistake it is there to catch.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import read_kv
+from ternary_weight_int8_amd import synth
+
+
+def page_table_weights():
+    """int8 weight of codes 0..3, read from the page's byte-permute table."""
+    t = read_kv("decode_table.txt")["perm_table"]
+    return np.array([(t >> (8 * c)) & 0xFF for c in range(4)], dtype=np.uint8).view(np.int8)
+
+
+def lut_decode(codes):
+    """Separate decode for the brute-force checks: page table indexed by code."""
+    return page_table_weights()[codes.astype(np.intp)]
+
+
+def codes_of_bytes_lsb_first(b):
+    """2-bit fields of each byte, first field in the low bits."""
+    b = np.asarray(b, dtype=np.uint8)
+    return np.stack([(b >> (2 * i)) & 3 for i in range(4)], axis=-1)
+
+
+# -- decode table (catches: wrong sign, code 3 treated as nonzero) ---------------
+
+def test_page_table_is_the_formula_table():
+    # two independent statements on the pages agree: 0,+1,-1,0
+    assert page_table_weights().tolist() == [0, 1, -1, 0]
+
+
+def test_oracle_weight_of_code_matches_page_table():
+    assert [oracle.weight_of_code(c) for c in range(4)] == page_table_weights().tolist()
+
+
+def test_decode_every_byte_matches_page_table():
+    Wp = np.arange(256, dtype=np.uint8).reshape(256, 1)       # N=256 rows, K=4
+    got = oracle.decode(Wp, 4)
+    want = lut_decode(codes_of_bytes_lsb_first(np.arange(256)))
+    np.testing.assert_array_equal(got, want)
+
+
+# -- packing (catches: bit order, row stride) -----------------------------------
+
+@pytest.mark.parametrize("byte,weights", [
+    (0x00, [0, 0, 0, 0]),
+    (0x01, [1, 0, 0, 0]),
+    (0x02, [-1, 0, 0, 0]),
+    (0x04, [0, 1, 0, 0]),
+    (0x40, [0, 0, 0, 1]),
+    (0x80, [0, 0, 0, -1]),
+    (0x06, [-1, 1, 0, 0]),
+    (0x55, [1, 1, 1, 1]),
+    (0xAA, [-1, -1, -1, -1]),
+    (0xFF, [0, 0, 0, 0]),
+    (0xC9, [1, -1, 0, 0]),
+])
+def test_hand_bytes(byte, weights):
+    got = oracle.decode(np.array([[byte]], dtype=np.uint8), 4)
+    assert got.tolist() == [weights]
+
+
+def test_pack_unpack_roundtrip_all_bytes():
+    Wp = np.arange(256, dtype=np.uint8).reshape(16, 16)       # N=16, K=64
+    codes = oracle.unpack(Wp, 64)
+    assert codes.max() <= 3
+    np.testing.assert_array_equal(oracle.pack(codes), Wp)
+
+
+def test_unpack_pack_roundtrip_random_codes():
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 4, size=(37, 52), dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.unpack(oracle.pack(codes), 52), codes)
+
+
+def test_row_stride_is_k_over_4():
+    # code (k, n) lives in byte n*(K/4) + k/4
+    N, K = 3, 12
+    codes = np.zeros((N, K), dtype=np.uint8)
+    codes[2, 9] = 1
+    Wp = oracle.pack(codes).reshape(-1)
+    assert np.flatnonzero(Wp).tolist() == [2 * (K // 4) + 9 // 4]
+    assert Wp[2 * 3 + 2] == 1 << (2 * (9 % 4))
+
+
+def test_generator_placement_agrees_with_oracle_pack():
+    codes = synth.random_codes(3, 29, 40, 4)
+    np.testing.assert_array_equal(synth.store_codes(codes), oracle.pack(codes))
+
+
+# -- forward: hand cases (catches: dropped term, transposed operand) ------------
+
+def test_fwd_hand_1x1x4():
+    # A = [3, -5, 7, 100]; codes 1, 2, 0, 3 -> weights +1, -1, 0, 0 -> 3 + 5 = 8
+    A = np.array([[3, -5, 7, 100]], dtype=np.int8)
+    Wp = np.array([[0xC9]], dtype=np.uint8)
+    assert oracle.fwd(A, Wp).tolist() == [[8]]
+
+
+def test_fwd_hand_2x3x8():
+    A = np.array([[1, 2, 3, 4, 5, 6, 7, 8],
+                  [-1, -2, -3, -4, -5, -6, -7, -8]], dtype=np.int8)
+    # n=0: all +1                       -> 36
+    # n=1: -1,-1,-1,-1, 0,0,0,0        -> -(1+2+3+4) = -10
+    # n=2: +1,-1,+1,-1, 0,0,0,0 (code 3) -> 1-2+3-4 = -2
+    Wp = np.array([[0x55, 0x55],
+                   [0xAA, 0x00],
+                   [0x99, 0xFF]], dtype=np.uint8)
+    assert oracle.fwd(A, Wp).tolist() == [[36, -10, -2], [-36, 10, 2]]
+
+
+# -- forward: closed forms -------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 4), (3, 5, 64), (7, 2, 1000)])
+def test_fwd_ones_times_plus_one_is_K(M, N, K):
+    A = np.ones((M, K), dtype=np.int8)
+    Wp = np.full((N, K // 4), 0x55, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.fwd(A, Wp), np.full((M, N), K))
+
+
+@pytest.mark.parametrize("byte,scale", [(0x55, -128), (0xAA, 128), (0x00, 0), (0xFF, 0)])
+def test_fwd_minus128_closed_forms(byte, scale):
+    M, N, K = 2, 3, 256
+    A = np.full((M, K), -128, dtype=np.int8)
+    Wp = np.full((N, K // 4), byte, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.fwd(A, Wp), np.full((M, N), scale * K))
+
+
+def test_fwd_swap_codes_negates():
+    A = synth.uniform_int8(11, 0, 9, 48)
+    codes = synth.random_codes(11, 7, 48, 4)
+    swapped = codes.copy()
+    swapped[codes == 1] = 2
+    swapped[codes == 2] = 1
+    C = oracle.fwd(A, synth.store_codes(codes))
+    Cs = oracle.fwd(A, synth.store_codes(swapped))
+    np.testing.assert_array_equal(Cs, -C)
+
+
+def test_fwd_row_sum_identity():
+    # sum_n C[m][n] = sum_k A[m][k] * (sum_n w(k, n))
+    A = synth.uniform_int8(5, 0, 6, 40)
+    codes = synth.random_codes(5, 9, 40, 4)
+    C = oracle.fwd(A, synth.store_codes(codes)).astype(np.int64)
+    colsum = lut_decode(codes).astype(np.int64).sum(axis=0)          # over n -> [K]
+    want = (A.astype(np.int64) * colsum[None, :]).sum(axis=1)
+    np.testing.assert_array_equal(C.sum(axis=1), want)
+
+
+# -- forward: brute force against numpy int64 matmul ------------------------------
+
+def test_fwd_exhaustive_code_columns():
+    # K=4, every one of the 256 possible code columns, A rows with the extremes
+    A = np.array([[-128, -128, -128, -128], [127, 127, 127, 127], [-128, 127, -1, 0],
+                  [1, 2, 3, 4], [0, 0, 0, 0], [-7, 19, -64, 99],
+                  [127, -128, 127, -128], [5, -5, 5, -5]], dtype=np.int8)
+    codes = codes_of_bytes_lsb_first(np.arange(256)).astype(np.uint8)   # [256][4]
+    Wp = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    want = A.astype(np.int64) @ lut_decode(codes).astype(np.int64).T
+    np.testing.assert_array_equal(oracle.fwd(A, Wp), want)
+
+
+@pytest.mark.parametrize("M,N,K,alphabet,seed", [
+    (1, 16, 16, 4, 1), (5, 3, 8, 4, 2), (17, 33, 96, 4, 3), (64, 7, 132, 3, 4), (2, 130, 260, 3, 5)])
+def test_fwd_brute_force(M, N, K, alphabet, seed):
+    A = synth.uniform_int8(seed, 0, M, K)
+    codes = synth.random_codes(seed, N, K, alphabet)
+    want = A.astype(np.int64) @ lut_decode(codes).astype(np.int64).T
+    np.testing.assert_array_equal(oracle.fwd(A, synth.store_codes(codes), threads=3), want)
+
+
+# -- forward: the int32 extremes (catches: int32 accumulation, missing overflow check)
+
+def test_fwd_int32_extremes_at_bound():
+    K = 16777212                            # largest multiple of 4 under 2^31/128
+    assert K <= read_kv("bounds.txt")["ternary_max_contraction"] < K + 4
+    A = np.full((1, K), -128, dtype=np.int8)
+    Wp = np.empty((2, K // 4), dtype=np.uint8)
+    Wp[0] = 0x55
+    Wp[1] = 0xAA
+    C, r = oracle.fwd(A, Wp, return_overflows=True)
+    assert r == 0
+    assert C.tolist() == [[-2147483136, 2147483136]]
+    assert C[0, 0] == np.iinfo(np.int32).min + 512
+    assert C[0, 1] == np.iinfo(np.int32).max - 511
+
+
+def test_fwd_overflow_detected_past_bound():
+    K = 1 << 24
+    A = np.full((1, K), -128, dtype=np.int8)
+    Wp = np.empty((2, K // 4), dtype=np.uint8)
+    Wp[0] = 0x55                            # -2^31 exactly: representable
+    Wp[1] = 0xAA                            # +2^31: not representable
+    C, r = oracle.fwd(A, Wp, allow_overflow=True, return_overflows=True)
+    assert r == 1
+    assert C[0, 0] == np.iinfo(np.int32).min
+    assert C[0, 1] == np.iinfo(np.int32).min   # wrapped low 32 bits of 2^31
+    with pytest.raises(oracle.OverflowInOracle):
+        oracle.fwd(A, Wp)
+
+
+def test_fwd_structured_halves_closed_form():
+    # the structured stress recipe, at a size the oracle does quickly
+    M, N, K = 64, 48, 4096
+    A, Wp = synth.extreme_inputs(2, M, N, K)
+    C = oracle.fwd(A, Wp)
+    s = np.where(np.arange(N) < N // 2, 1, -1)
+    rowsum = A.astype(np.int64).sum(axis=1)
+    np.testing.assert_array_equal(C, rowsum[:, None] * s[None, :])
+    assert (C[: M // 2, : N // 2] == -128 * K).all()
+
+
+# -- dX (catches: contraction over the wrong index, layout of the shared W) --------
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 4, 16, 1), (9, 12, 20, 2), (27, 64, 96, 3), (5, 200, 8, 4)])
+def test_dx_brute_force(M, N, K, seed):
+    dC = synth.uniform_int8(seed, 2, M, N)
+    codes = synth.random_codes(seed, N, K, 3)
+    want = dC.astype(np.int64) @ lut_decode(codes).astype(np.int64)     # [M][N] x [N][K]
+    np.testing.assert_array_equal(oracle.dx(dC, synth.store_codes(codes), K), want)
+
+
+def test_dx_hand():
+    # W (K=4 x N=2): n=0 codes 1,2,0,3 -> w(.,0) = +1,-1,0,0 ; n=1 all +1
+    Wp = np.array([[0xC9], [0x55]], dtype=np.uint8)
+    dC = np.array([[10, -3]], dtype=np.int8)
+    # dX[k] = 10*w(k,0) - 3*w(k,1) = [10-3, -10-3, -3, -3]
+    assert oracle.dx(dC, Wp, 4).tolist() == [[7, -13, -3, -3]]
+
+
+def test_dx_is_forward_on_transposed_weights():
+    M, N, K = 6, 24, 40
+    dC = synth.uniform_int8(8, 2, M, N)
+    codes = synth.random_codes(8, N, K, 4)               # [N][K]
+    WpT = oracle.pack(np.ascontiguousarray(codes.T))     # codes along N, rows k
+    np.testing.assert_array_equal(oracle.dx(dC, synth.store_codes(codes), K),
+                                  oracle.fwd(dC, WpT))
+
+
+# -- dW ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 1, 1), (27, 16, 12, 2), (300, 33, 17, 3), (1782, 5, 7, 4)])
+def test_dw_brute_force(M, N, K, seed):
+    A = synth.uniform_int8(seed, 0, M, K)
+    dC = synth.uniform_int8(seed, 2, M, N)
+    want = A.astype(np.int64).T @ dC.astype(np.int64)
+    np.testing.assert_array_equal(oracle.dw(A, dC, threads=4), want)
+
+
+def test_dw_hand():
+    A = np.array([[1, -2], [3, 4], [-5, 6]], dtype=np.int8)      # M=3, K=2
+    dC = np.array([[7], [-1], [2]], dtype=np.int8)               # M=3, N=1
+    # dW[0] = 1*7 + 3*(-1) + (-5)*2 = -6 ; dW[1] = -2*7 + 4*(-1) + 6*2 = -6
+    assert oracle.dw(A, dC).tolist() == [[-6], [-6]]
+
+
+def test_dw_int32_extremes_at_bound():
+    M = read_kv("bounds.txt")["dw_max_contraction"]
+    assert M == (2**31 - 1) // (128 * 128)
+    A = np.full((M, 1), -128, dtype=np.int8)
+    dC = np.empty((M, 2), dtype=np.int8)
+    dC[:, 0] = -128
+    dC[:, 1] = 127
+    dW, r = oracle.dw(A, dC, return_overflows=True)
+    assert r == 0
+    assert dW.tolist() == [[2147467264, -2130690176]]
+
+
+def test_dw_overflow_detected_past_bound():
+    M = read_kv("bounds.txt")["dw_max_contraction"] + 1
+    A = np.full((M, 1), -128, dtype=np.int8)
+    dC = np.full((M, 1), -128, dtype=np.int8)
+    _, r = oracle.dw(A, dC, allow_overflow=True, return_overflows=True)
+    assert r == 1
+
+
+# -- threading does not change the result ---------------------------------------
+
+def test_thread_count_invariance():
+    A, Wp = synth.fwd_inputs(21, 37, 19, 64, 4)
+    base = oracle.fwd(A, Wp, threads=1)
+    for t in (2, 5, 64):
+        np.testing.assert_array_equal(oracle.fwd(A, Wp, threads=t), base)
+    dC = synth.uniform_int8(21, 2, 37, 19)
+    np.testing.assert_array_equal(oracle.dw(A, dC, threads=1), oracle.dw(A, dC, threads=7))
+    np.testing.assert_array_equal(oracle.dx(dC, Wp, 64, threads=1), oracle.dx(dC, Wp, 64, threads=6))
+
+
+def test_negative_overflow_detected():
+    # below INT32_MIN: fwd with -128 x (+1) at K = 2^24 + 4, and dW with
+    # -128 x 127 summed over 132105 rows (-16256 * 132105 = -2147498880)
+    K = (1 << 24) + 4
+    A = np.full((1, K), -128, dtype=np.int8)
+    Wp = np.full((1, K // 4), 0x55, dtype=np.uint8)
+    _, r = oracle.fwd(A, Wp, allow_overflow=True, return_overflows=True)
+    assert r == 1
+    M = 132105
+    A = np.full((M, 1), -128, dtype=np.int8)
+    dC = np.full((M, 1), 127, dtype=np.int8)
+    dW, r = oracle.dw(A, dC, allow_overflow=True, return_overflows=True)
+    assert r == 1
+    assert int(dW[0, 0]) == -2147498880 + 2**32
