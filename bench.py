@@ -1,0 +1,237 @@
+"""Benchmark of the ternary x int8 GEMM hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input at
+M=16384, N=3456, K=1280 (the "500m" throughput shape):
+    forward  C  = A x W          int8 x ternary (2-bit packed) -> int32
+    dX       dX = dC x W^T       same stored W
+    dW       dW = A^T x dC       int8 x int8 -> int32, contraction over M
+Inputs are resident in HBM before the timed region.  W steps run untimed, then
+K steps are timed between HIP events on the stream the kernels run on, with a
+device synchronisation on both sides; each kernel is also bracketed by its own
+events to give its average launch duration.  One JSON line goes to stdout.
+
+Work is counted as 2*M*N*K ops per product (zero weights included: the method
+computes densely).  Peaks are AMD's published MI355X figures.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ternary x int8 GEMM TOPS at 16384x3456x1280; % of int8 MFMA peak"
+PEAK_INT8_OPS = 5.0e15      # dense int8 MFMA, ops/s
+PEAK_HBM_BPS = 8.0e12       # HBM3E, bytes/s
+RIDGE = PEAK_INT8_OPS / PEAK_HBM_BPS
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_work(name, M, N, K):
+    """(ops, algorithmic HBM bytes) of one launch: each operand read once, output written once."""
+    ops = 2 * M * N * K
+    if name == "fwd":
+        byts = M * K + N * (K // 4) + 4 * M * N
+    elif name == "dx":
+        byts = M * N + N * (K // 4) + 4 * M * K
+    else:
+        byts = M * K + M * N + 4 * K * N
+    return ops, byts
+
+
+def source_digest():
+    src = os.path.join(ROOT, "ternary_weight_int8_amd", "csrc", "ternary_gemm.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(kernel, workload_tag):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_tag}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit():
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(A, Wp, dC, K, rows):
+    """The oracle as it stands, on the first `rows` rows of the same batch."""
+    import oracle  # CPU baseline leg only
+
+    threads = cpu_threads()
+    a, g = np.ascontiguousarray(A[:rows]), np.ascontiguousarray(dC[:rows])
+    N = Wp.shape[0]
+    t0 = time.perf_counter()
+    oracle.fwd(a, Wp, threads=threads)
+    oracle.dx(g, Wp, K, threads=threads)
+    oracle.dw(a, g, threads=threads)
+    dt = time.perf_counter() - t0
+    ops = 3 * 2 * rows * N * K
+    return {
+        "value": ops / dt / 1e12,
+        "unit": "TOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"forward + dX + dW on the first {rows} of the 16384 rows "
+                  f"({rows}x{N}x{K} each, same inputs), {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the batch the CPU oracle baseline runs on (0: skip)")
+    ap.add_argument("--only", choices=["fwd", "dx", "dw"], default=None,
+                    help="time a single product instead of the whole step (for profiling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_int8_amd import binding as B
+    from ternary_weight_int8_amd import synth
+
+    B.lib()  # fail loudly now if the library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c = synth.CONFIGS["large"]
+    M, N, K = c["M"], c["N"], c["K"]
+    A, Wp = synth.fwd_inputs(args.seed, M, N, K, c["alphabet"])
+    dC = synth.uniform_int8(args.seed, synth.STREAM_DC, M, N)
+
+    Ad = torch.from_numpy(A).to(dev)
+    Wd = torch.from_numpy(Wp).to(dev)
+    dCd = torch.from_numpy(dC).to(dev)
+    Cd = torch.empty((M, N), dtype=torch.int32, device=dev)
+    dXd = torch.empty((M, K), dtype=torch.int32, device=dev)
+    dWd = torch.empty((K, N), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    launches = {
+        "fwd": lambda: B.ternary_gemm_s8(Ad, Wd, C=Cd, stream=stream),
+        "dx": lambda: B.ternary_gemm_s8_dx(dCd, Wd, K, dX=dXd, stream=stream),
+        "dw": lambda: B.ternary_gemm_s8_dw(Ad, dCd, dW=dWd, stream=stream),
+    }
+    names = [args.only] if args.only else ["fwd", "dx", "dw"]
+
+    for _ in range(args.warmup):
+        for n in names:
+            launches[n]()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, n in enumerate(names):
+            launches[n]()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    total_ms = ev[0][0].elapsed_time(ev[-1][-1])
+    per = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+    ms_per_step = total_ms / args.steps
+
+    tag = f"{M}x{N}x{K}"
+    kernels = {}
+    for n in names:
+        ops, byts = kernel_work(n, M, N, K)
+        t = per[n] / 1e3
+        kernels[n] = {
+            "avg_us": per[n] * 1e3,
+            "tops": ops / t / 1e12,
+            "mfma_frac": ops / t / PEAK_INT8_OPS,
+            "gbps": byts / t / 1e9,
+            "hbm_frac": byts / t / PEAK_HBM_BPS,
+            "bound": "hbm" if ops / byts < RIDGE else "mfma",
+            "algorithmic_bytes": byts,
+            "ops": ops,
+        }
+    kernels["fwd_context"] = {"pages_rtx4090_fwd_tops": 171,
+                              "note": "the pages' forward at this shape on another vendor's GPU"}
+
+    dominant = max(names, key=lambda n: per[n])
+    d = kernels[dominant]
+    if d["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": d["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                "frac": d["hbm_frac"]}
+    else:
+        roof = {"bound": "mfma", "achieved": d["tops"], "peak": PEAK_INT8_OPS / 1e12,
+                "unit": "TFLOP/s", "frac": d["mfma_frac"]}
+    roof["kernel"] = dominant
+    roof["traffic"] = recorded_traffic(dominant, tag)
+
+    total_ops = sum(kernel_work(n, M, N, K)[0] for n in names)
+    value = total_ops * args.steps / (total_ms / 1e3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "wall_ms_per_step": t_wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": ("ternary x int8 GEMM hot path, "
+                         + " + ".join({"fwd": "forward", "dx": "dX", "dw": "dW"}[n] for n in names)
+                         + f" at M={M} N={N} K={K}"),
+            "M": M, "N": N, "K": K, "seed": args.seed,
+            "A": "int8 uniform [-128,127]", "W": "2-bit codes uniform over {0,1,2}",
+            "dC": "int8 uniform [-128,127]",
+        },
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:
+        line["cpu_baseline"] = cpu_baseline(A, Wp, dC, K, min(args.cpu_rows, M))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

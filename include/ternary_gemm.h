@@ -1,0 +1,145 @@
+/*
+ * ternary_gemm.h -- C ABI of the MI355X (gfx950) ternary x int8 GEMM library
+ * (libternary_gemm.so).
+ *
+ * Sources (cited by page title and section):
+ *   [P10425] t27 pull request #10425, "t27c PTX backend: ternary x int8 GEMM
+ *            kernel emitted by a .t27 spec (int8 mma.sync), ptx-run glue".
+ *   [P10855] t27 pull request #10855, "spec(igla): hslm_bwd_ptx -- HSLM
+ *            backward dX and dW as int8 tensor-core PTX written by t27".
+ *
+ * Stored ternary weights ("Wpacked").  W is a K x N matrix of weights in
+ * {-1, 0, +1} kept as 2-bit codes, four per byte, one row of K/4 bytes per
+ * output column n (N-major, the code index of (k, n) being n*K + k) [P10425
+ * "What this adds"; P10855 PR body].  The code of (k, n) sits in byte
+ * n*(K/4) + k/4 at bits 2*(k%4) and 2*(k%4)+1, the first code of a byte in the
+ * least significant bits (the pages do not state the order inside a byte;
+ * this is the reading taken).  A code c stands for the weight
+ * (c & 1) - ((c >> 1) & 1): codes 0, 1, 2, 3 are 0, +1, -1, 0 [P10425 "What
+ * this adds"; the same table appears as the byte-permute word 0x00FF0100 in
+ * P10855 PR body].
+ *
+ * Conventions shared by every call:
+ *   - All matrix arguments are DEVICE pointers to dense row-major storage with
+ *     no padding between rows; the caller owns them.  The library allocates,
+ *     frees, copies and retains nothing.
+ *   - No alignment beyond the element size is required; aligned bases and
+ *     row lengths that are multiples of 16 take the fast load path.
+ *   - Each call validates its arguments on the host first.  On any error it
+ *     returns a negative status, launches nothing and leaves every output
+ *     untouched.
+ *   - On success the work is enqueued on `stream` (NULL: the default stream)
+ *     and the call returns without waiting.  Faults that only show while the
+ *     kernel runs surface at the caller's next synchronisation.
+ *   - Results are exact: integer sums in int32, each output reduced serially
+ *     over the whole contraction inside one workgroup (no split of the
+ *     contraction, no atomics), so repeated calls give identical bits.
+ *   - Calls are thread-safe; concurrent calls on different streams may run at
+ *     the same time as long as their outputs do not overlap.
+ */
+#ifndef TERNARY_GEMM_H
+#define TERNARY_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum tgemm_status {
+    TGEMM_OK = 0,
+    TGEMM_ERR_NULL = -1,   /* a required pointer is NULL                        */
+    TGEMM_ERR_DIM = -2,    /* a dimension is < 1, or a size does not fit        */
+    TGEMM_ERR_PACK = -3,   /* the packed dimension K is not a multiple of 4     */
+    TGEMM_ERR_BOUND = -4,  /* the contraction is longer than the exact-int32 bound */
+    TGEMM_ERR_ALIAS = -5,  /* the output overlaps an input                       */
+    TGEMM_ERR_HIP = -6     /* the HIP runtime reported an error at launch        */
+} tgemm_status;
+
+/* Longest contraction for which every int32 result is exact whatever the
+ * inputs.  Ternary x int8 (forward, dX): |sum| <= 128 * L must fit int32,
+ * L <= floor((2^31 - 1) / 128) [P10425 "What this adds", invariant "i32
+ * overflow bound"].  int8 x int8 (dW): L <= floor((2^31 - 1) / 128^2) = 131071
+ * [P10855 PR body, kernel 2, "k <= 131071"]. */
+#define TGEMM_TERNARY_MAX_CONTRACTION 16777215LL
+#define TGEMM_INT8_MAX_CONTRACTION 131071LL
+
+/*
+ * Forward product [P10425 "What this adds"]:
+ *     C[m][n] = sum_{k<K} A[m][k] * w(k, n)
+ *   A        int8    [M][K]
+ *   Wpacked  uint8   [N][K/4]   (stored ternary weights, layout above)
+ *   C        int32   [M][N]     (written, never read)
+ * Requires M, N, K >= 1, K % 4 == 0 (TGEMM_ERR_PACK otherwise) and
+ * K <= TGEMM_TERNARY_MAX_CONTRACTION (TGEMM_ERR_BOUND).
+ */
+int ternary_gemm_s8(const int8_t *A, const uint8_t *Wpacked, int32_t *C,
+                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * dX = dC x W^T with the same stored ternary W as the forward product
+ * [P10855 PR body, kernel 1 "hslm_dx_s8"]:
+ *     dX[m][k] = sum_{n<N} dC[m][n] * w(k, n)
+ *   dC       int8    [M][N]
+ *   Wpacked  uint8   [N][K/4]   (the forward call's buffer, unchanged)
+ *   dX       int32   [M][K]     (written, never read)
+ * Requires M, N, K >= 1, K % 4 == 0 (TGEMM_ERR_PACK) and
+ * N <= TGEMM_TERNARY_MAX_CONTRACTION (TGEMM_ERR_BOUND).
+ */
+int ternary_gemm_s8_dx(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * dW = A^T x dC, int8 x int8 -> int32, summed over the M rows
+ * [P10855 PR body, kernel 2 "hslm_dw_s8"]:
+ *     dW[k][n] = sum_{m<M} A[m][k] * dC[m][n]
+ *   A        int8    [M][K]
+ *   dC       int8    [M][N]
+ *   dW       int32   [K][N]     (written, never read)
+ * Requires M, N, K >= 1 and M <= TGEMM_INT8_MAX_CONTRACTION (TGEMM_ERR_BOUND).
+ * K need not be a multiple of 4 (no packed operand).
+ */
+int ternary_gemm_s8_dw(const int8_t *A, const int8_t *dC, int32_t *dW,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *ternary_gemm_status_str(int status);
+
+/*
+ * Launch plan the library would use for a call, computed on the host without
+ * touching the device (for tests and tooling).  op: 0 forward, 1 dX, 2 dW.
+ * Fills the output tile (rows x cols of the row-major output per workgroup),
+ * the number of workgroups, the LDS bytes per workgroup and whether the fast
+ * (vector-load) path applies given the base alignments passed in `align`
+ * (the smallest power-of-two alignment of the input pointers, in bytes).
+ * Returns TGEMM_OK, or the status the real call would return for these
+ * dimensions (pointer checks excepted).
+ */
+typedef struct tgemm_plan {
+    int64_t out_rows, out_cols, contraction;
+    int32_t tile_rows, tile_cols;
+    int64_t workgroups;
+    int32_t threads_per_workgroup;
+    int32_t lds_bytes;
+    int32_t fast_path;
+} tgemm_plan;
+
+int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align,
+                      tgemm_plan *plan);
+
+/*
+ * Output tile handled by workgroup `block` under a plan (host mirror of the
+ * kernel's own block -> tile order, which keeps the tiles that share input rows
+ * on one of the chip's eight L2 slices).  Writes the tile's first output row
+ * and column.  Returns TGEMM_OK or TGEMM_ERR_DIM if block is out of range.
+ */
+int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block,
+                               int64_t *row0, int64_t *col0);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERNARY_GEMM_H */

@@ -57,7 +57,13 @@ def _load():
 
 
 def default_threads() -> int:
-    return os.cpu_count() or 1
+    """Threads for the oracle: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when set (the share a job is given on a shared host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _ptr(a: np.ndarray):

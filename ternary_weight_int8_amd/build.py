@@ -1,0 +1,37 @@
+"""Build libternary_gemm.so in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "ternary_gemm.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libternary_gemm.so")
+ARCH = "gfx950"
+
+
+def hipcc_cmd(out: str) -> list[str]:
+    return [
+        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # no packed-fp32 instructions in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, SRC, "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the HIP library (always) and atomically replace the old one."""
+    tmp = LIB + ".tmp"
+    r = subprocess.run(hipcc_cmd(tmp), capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    if verbose:
+        print(r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,154 @@
+"""The C-ABI library on a host without a GPU: exports, validation, launch plan.
+
+Validation runs before any HIP call, so every error path here is exercised
+without a device and without launching anything.
+"""
+import os
+import re
+
+import pytest
+
+from ternary_weight_int8_amd import binding as B
+from golden_io import read_kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
+
+GEMMS = ("ternary_gemm_s8", "ternary_gemm_s8_dx", "ternary_gemm_s8_dw")
+FAKE = (0x10000, 0x20000000, 0x40000000)    # three distinct, never-dereferenced addresses
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in (B.OK, B.ERR_NULL, B.ERR_DIM, B.ERR_PACK, B.ERR_BOUND, B.ERR_ALIAS, B.ERR_HIP):
+        s = B.status_str(st)
+        assert s and s != "unknown status"
+    assert B.status_str(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("name", GEMMS)
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_null_pointer_rejected(name, which):
+    ptrs = list(FAKE)
+    ptrs[which] = None
+    assert B.call_raw(name, *ptrs, 4, 4, 4) == B.ERR_NULL
+
+
+@pytest.mark.parametrize("name", GEMMS)
+@pytest.mark.parametrize("dims", [(0, 4, 4), (4, 0, 4), (4, 4, 0), (-1, 4, 4), (1 << 40, 1 << 40, 4)])
+def test_bad_dims_rejected(name, dims):
+    assert B.call_raw(name, *FAKE, *dims) == B.ERR_DIM
+
+
+@pytest.mark.parametrize("name", GEMMS[:2])
+@pytest.mark.parametrize("K", [1, 2, 3, 6, 97])
+def test_packed_dim_must_be_multiple_of_4(name, K):
+    assert B.call_raw(name, *FAKE, 3, 5, K) == B.ERR_PACK
+
+
+def test_dw_needs_no_packing():
+    # K % 4 != 0 is fine for dW; with these fake pointers the call gets as far
+    # as the launch only on a GPU host, so compare with the plan instead
+    assert B.plan("dw", 3, 5, 7).out_rows == 7
+
+
+def test_contraction_bounds():
+    b = read_kv("bounds.txt")
+    tern, i8 = b["ternary_max_contraction"], b["dw_max_contraction"]
+    # forward: contraction K; largest multiple of 4 under the bound passes the check
+    assert B.plan("fwd", 1, 1, tern - tern % 4).contraction == tern - tern % 4
+    assert B.call_raw("ternary_gemm_s8", *FAKE, 1, 1, tern + 1 + (4 - (tern + 1) % 4) % 4) == B.ERR_BOUND
+    # dX: contraction N
+    assert B.plan("dx", 1, tern, 4).contraction == tern
+    assert B.call_raw("ternary_gemm_s8_dx", *FAKE, 1, tern + 1, 4) == B.ERR_BOUND
+    # dW: contraction M
+    assert B.plan("dw", i8, 1, 1).contraction == i8
+    assert B.call_raw("ternary_gemm_s8_dw", *FAKE, i8 + 1, 1, 1) == B.ERR_BOUND
+
+
+def test_alias_rejected():
+    base = 0x100000
+    M, N, K = 8, 8, 16
+    # output starts inside A
+    assert B.call_raw("ternary_gemm_s8", base, base + 4096, base + 8, M, N, K) == B.ERR_ALIAS
+    # output covers Wpacked
+    assert B.call_raw("ternary_gemm_s8", base, base + 4096, base + 4000, M, N, K) == B.ERR_ALIAS
+    assert B.call_raw("ternary_gemm_s8_dx", base, base + 4096, base + 4096 + 16, M, N, K) == B.ERR_ALIAS
+    assert B.call_raw("ternary_gemm_s8_dw", base, base + 4096, base + 4096, M, N, K) == B.ERR_ALIAS
+
+
+def _coverage(op, M, N, K):
+    pl = B.plan(op, M, N, K)
+    seen = set()
+    for blk in range(pl.workgroups):
+        r0, c0 = B.tile_of_block(pl, blk)
+        assert r0 % pl.tile_rows == 0 and c0 % pl.tile_cols == 0
+        assert 0 <= r0 < pl.out_rows and 0 <= c0 < pl.out_cols
+        seen.add((r0, c0))
+    want = {(r, c) for r in range(0, pl.out_rows, pl.tile_rows)
+            for c in range(0, pl.out_cols, pl.tile_cols)}
+    assert seen == want and len(seen) == pl.workgroups
+    return pl
+
+
+@pytest.mark.parametrize("op,M,N,K", [
+    ("fwd", 1, 16, 16), ("fwd", 300, 272, 96), ("fwd", 16384, 3456, 1280),
+    ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
+    ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)])
+def test_every_output_tile_covered_once(op, M, N, K):
+    pl = _coverage(op, M, N, K)
+    assert pl.threads_per_workgroup == 256
+    assert pl.lds_bytes <= 160 * 1024
+
+
+def test_block_out_of_range():
+    pl = B.plan("fwd", 300, 272, 96)
+    with pytest.raises(B.TernaryGemmError):
+        B.tile_of_block(pl, pl.workgroups)
+
+
+def test_same_xcd_tiles_share_rows():
+    # workgroups b and b+8 run on the same XCD; in the headline plan they take
+    # neighbouring tiles along the output columns of the same row panel
+    pl = B.plan("fwd", 16384, 3456, 1280)
+    same_rows = 0
+    for b in range(0, 512):
+        r0, c0 = B.tile_of_block(pl, b)
+        r1, c1 = B.tile_of_block(pl, b + 8)
+        same_rows += (r0 == r1)
+    assert same_rows >= 0.9 * 512
+
+
+def test_headline_plan():
+    pl = B.plan("fwd", 16384, 3456, 1280)
+    assert (pl.tile_rows, pl.tile_cols) == (256, 128)
+    assert pl.workgroups == 64 * 27
+    assert pl.fast_path == 1
+    assert B.plan("fwd", 16384, 3456, 1280, align=2).fast_path == 0
+    assert B.plan("fwd", 300, 272, 96).fast_path == 1        # 96 % 16 == 0
+    assert B.plan("fwd", 300, 272, 100).fast_path == 0
+
+
+def test_wrappers_refuse_host_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros((4, 16), dtype=torch.int8)
+    Wp = torch.zeros((4, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        B.ternary_gemm_s8(A, Wp)
+    with pytest.raises(TypeError):
+        B.ternary_gemm_s8(A.to(torch.int16), Wp)

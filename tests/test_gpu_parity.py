@@ -1,0 +1,267 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+All products are exact integer results, so the bar is bit-exact equality
+(mismatch count 0) on every seeded input.  The oracle computes every element
+of every case here, the 16384 x 3456 x 1280 forward included; the structured
+2048 x 2048 x 65536 stress case is checked in full against its closed form and
+on sampled rows against the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_int8_amd import binding as B
+from ternary_weight_int8_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_exact(got, want, what):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    if len(bad):
+        first = [(tuple(int(v) for v in ix), int(got[tuple(ix)]), int(want[tuple(ix)])) for ix in bad[:8]]
+        pytest.fail(f"{what}: {len(bad)} mismatches of {got.size}; first (index, gpu, oracle): {first}")
+
+
+def gpu_fwd(A, Wp):
+    return host(B.ternary_gemm_s8(dev(A), dev(Wp)))
+
+
+def gpu_dx(dC, Wp, K):
+    return host(B.ternary_gemm_s8_dx(dev(dC), dev(Wp), K))
+
+
+def gpu_dw(A, dC):
+    return host(B.ternary_gemm_s8_dw(dev(A), dev(dC)))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(16))
+def test_tiny(seed):
+    c = synth.CONFIGS["tiny"]
+    say(f"tiny seed={seed}")
+    A, Wp = synth.fwd_inputs(seed, c["M"], c["N"], c["K"], c["alphabet"])
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"tiny seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_ragged(seed):
+    c = synth.CONFIGS["ragged"]
+    say(f"ragged seed={seed}")
+    A, Wp = synth.fwd_inputs(seed, c["M"], c["N"], c["K"], c["alphabet"])
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"ragged seed {seed}")
+
+
+@pytest.fixture(scope="module")
+def large_inputs():
+    c = synth.CONFIGS["large"]
+    return synth.fwd_inputs(1, c["M"], c["N"], c["K"], c["alphabet"])
+
+
+def test_large_full(large_inputs):
+    say("large 16384x3456x1280 seed=1, every element")
+    A, Wp = large_inputs
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), "large seed 1")
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_large_other_seeds(seed):
+    # every 7th row plus the last row and every row of the first tile row,
+    # against the oracle; the whole tensor against the row- and column-sum
+    # identities, which hold for the exact product at any size
+    c = synth.CONFIGS["large"]
+    M, N, K = c["M"], c["N"], c["K"]
+    say(f"large seed={seed}, sampled rows + sum identities")
+    A, Wp = synth.fwd_inputs(seed, M, N, K, c["alphabet"])
+    C = gpu_fwd(A, Wp)
+    rows = np.unique(np.concatenate([np.arange(0, M, 7), np.arange(256), [M - 1]]))
+    assert_exact(C[rows], oracle.fwd(A[rows], Wp), f"large seed {seed} rows")
+    w = oracle.decode(Wp, K).astype(np.int64)              # [N][K]
+    A64 = A.astype(np.int64)
+    np.testing.assert_array_equal(C.astype(np.int64).sum(axis=1), A64 @ w.sum(axis=0))
+    np.testing.assert_array_equal(C.astype(np.int64).sum(axis=0), w @ A64.sum(axis=0))
+
+
+def test_extreme():
+    c = synth.CONFIGS["extreme"]
+    M, N, K = c["M"], c["N"], c["K"]
+    say("extreme 2048x2048x65536 closed form + sampled rows")
+    A, Wp = synth.extreme_inputs(1, M, N, K)
+    C = gpu_fwd(A, Wp)
+    sign = np.where(np.arange(N) < N // 2, 1, -1).astype(np.int64)
+    want = A.astype(np.int64).sum(axis=1)[:, None] * sign[None, :]
+    assert_exact(C.astype(np.int64), want, "extreme closed form")
+    assert (C[: M // 2, : N // 2] == -128 * K).all() and (C[: M // 2, N // 2:] == 128 * K).all()
+    rows = np.array([0, 1, M // 2 - 1, M // 2, M // 2 + 1, M - 2, M - 1])
+    assert_exact(C[rows], oracle.fwd(A[rows], Wp), "extreme rows vs oracle")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_backward_pair(seed):
+    c = synth.CONFIGS["backward"]
+    M, N, K = c["M"], c["N"], c["K"]
+    say(f"backward dX seed={seed}")
+    dC, Wp = synth.dx_inputs(seed, M, N, K, c["alphabet"])
+    assert_exact(gpu_dx(dC, Wp, K), oracle.dx(dC, Wp, K), f"dX seed {seed}")
+    say(f"backward dW seed={seed}")
+    A, dC2 = synth.dw_inputs(seed, M, N, K)
+    assert_exact(gpu_dw(A, dC2), oracle.dw(A, dC2), f"dW seed {seed}")
+
+
+# ---------------------------------------------------------------------------
+# every tile shape x load path, with ragged edges in all three dimensions
+# ---------------------------------------------------------------------------
+
+FWD_SHAPES = [  # (M, N, K): large / medium / small tile, fast (K%16==0) and slow
+    (4100, 3900, 80), (4100, 3900, 84), (2100, 3900, 80), (2100, 3900, 52),
+    (300, 272, 96), (299, 271, 100), (1, 1, 4), (1, 4097, 36), (1000, 1, 64), (65, 65, 68)]
+DX_SHAPES = [  # (M, N, K): contraction N
+    (4100, 80, 3900), (4100, 84, 3900), (2100, 80, 3900), (2100, 36, 3900),
+    (300, 96, 272), (299, 100, 268), (1, 1, 4), (27, 3456, 1280), (1, 4, 4100)]
+DW_SHAPES = [  # (M, N, K): contraction M
+    (80, 3900, 4100), (81, 3901, 4101), (80, 3900, 2100), (19, 3903, 2101),
+    (96, 272, 300), (97, 271, 299), (1, 1, 1), (1782, 5, 7), (27, 3456, 1280)]
+
+
+def tile_of(op, M, N, K):
+    pl = B.plan(op, M, N, K)
+    return pl.tile_rows, pl.tile_cols, pl.fast_path
+
+
+def test_shape_lists_reach_every_tile_and_path():
+    for op, shapes in (("fwd", FWD_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
+        seen = {tile_of(op, *s) for s in shapes}
+        for tile in ((256, 128), (128, 128), (64, 64)):
+            for fast in (0, 1):
+                assert (*tile, fast) in seen, (op, tile, fast)
+
+
+@pytest.mark.parametrize("M,N,K", FWD_SHAPES)
+def test_fwd_shapes(M, N, K):
+    say(f"fwd {M}x{N}x{K} plan={tile_of('fwd', M, N, K)}")
+    A, Wp = synth.fwd_inputs(M * 7 + K, M, N, K, 4)
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", DX_SHAPES)
+def test_dx_shapes(M, N, K):
+    say(f"dx {M}x{N}x{K} plan={tile_of('dx', M, N, K)}")
+    dC, Wp = synth.dx_inputs(M * 5 + N, M, N, K, 4)
+    assert_exact(gpu_dx(dC, Wp, K), oracle.dx(dC, Wp, K), f"dx {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", DW_SHAPES)
+def test_dw_shapes(M, N, K):
+    say(f"dw {M}x{N}x{K} plan={tile_of('dw', M, N, K)}")
+    A, dC = synth.dw_inputs(M * 3 + K, M, N, K)
+    assert_exact(gpu_dw(A, dC), oracle.dw(A, dC), f"dw {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# alignment, coverage, determinism
+# ---------------------------------------------------------------------------
+
+def offset_view(x_np, offset):
+    """Device copy of x starting `offset` bytes into a fresh buffer (misaligned base)."""
+    flat = np.ascontiguousarray(x_np).reshape(-1).view(np.uint8)
+    buf = torch.zeros(flat.size + 64, dtype=torch.uint8, device=DEV)
+    buf[offset:offset + flat.size] = torch.from_numpy(flat).to(DEV)
+    v = buf[offset:offset + flat.size]
+    return v.view(torch.int8 if x_np.dtype == np.int8 else torch.uint8).view(*x_np.shape)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4, 8])
+def test_misaligned_bases(offset):
+    M, N, K = 300, 272, 96
+    say(f"misaligned by {offset}")
+    A, Wp = synth.fwd_inputs(offset, M, N, K, 4)
+    Ad, Wd = offset_view(A, offset), offset_view(Wp, offset)
+    assert Ad.data_ptr() % 16 != 0
+    assert_exact(host(B.ternary_gemm_s8(Ad, Wd)), oracle.fwd(A, Wp), "fwd misaligned")
+    dC = synth.uniform_int8(offset, 2, M, N)
+    assert_exact(host(B.ternary_gemm_s8_dx(offset_view(dC, offset), Wd, K)),
+                 oracle.dx(dC, Wp, K), "dx misaligned")
+    assert_exact(host(B.ternary_gemm_s8_dw(Ad, offset_view(dC, offset))),
+                 oracle.dw(A, dC), "dw misaligned")
+
+
+@pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 3900, 80),
+                                      ("dx", 299, 100, 268), ("dw", 97, 271, 299)])
+def test_writes_exactly_the_output(op, M, N, K):
+    # the output sits between two canary bands inside one buffer, pre-filled
+    # with a sentinel no result here can take; afterwards every output element
+    # is written and no canary changed
+    say(f"canary {op} {M}x{N}x{K}")
+    R, Cc = {"fwd": (M, N), "dx": (M, K), "dw": (K, N)}[op]
+    band = 4096 + 3
+    sentinel, canary = 0x7FFFFFFF, -0x2A2A2A2B
+    buf = torch.full((band + R * Cc + band,), canary, dtype=torch.int32, device=DEV)
+    out = buf[band:band + R * Cc].view(R, Cc)
+    out.fill_(sentinel)
+    if op == "fwd":
+        A, Wp = synth.fwd_inputs(9, M, N, K, 4)
+        B.ternary_gemm_s8(dev(A), dev(Wp), C=out)
+        want = oracle.fwd(A, Wp)
+    elif op == "dx":
+        dC, Wp = synth.dx_inputs(9, M, N, K, 4)
+        B.ternary_gemm_s8_dx(dev(dC), dev(Wp), K, dX=out)
+        want = oracle.dx(dC, Wp, K)
+    else:
+        A, dC = synth.dw_inputs(9, M, N, K)
+        B.ternary_gemm_s8_dw(dev(A), dev(dC), dW=out)
+        want = oracle.dw(A, dC)
+    b = host(buf)
+    assert (b[:band] == canary).all() and (b[band + R * Cc:] == canary).all()
+    assert not (b[band:band + R * Cc] == sentinel).any()
+    assert_exact(b[band:band + R * Cc].reshape(R, Cc), want, "canary case")
+
+
+def test_deterministic_and_stream_independent():
+    c = synth.CONFIGS["backward"]
+    M, N, K = c["M"], c["N"], c["K"]
+    say("determinism")
+    A, Wp = synth.fwd_inputs(5, M, N, K, 3)
+    Ad, Wd = dev(A), dev(Wp)
+    first = B.ternary_gemm_s8(Ad, Wd).clone()
+    s = torch.cuda.Stream()
+    for _ in range(3):
+        again = B.ternary_gemm_s8(Ad, Wd)
+        assert torch.equal(first, again)
+    with torch.cuda.stream(s):
+        other = B.ternary_gemm_s8(Ad, Wd, stream=s)
+    s.synchronize()
+    assert torch.equal(first, other)
+
+
+def test_shape_errors_raise():
+    A = torch.zeros((4, 16), dtype=torch.int8, device=DEV)
+    with pytest.raises(ValueError):
+        B.ternary_gemm_s8(A, torch.zeros((4, 5), dtype=torch.uint8, device=DEV))
+    A6 = torch.zeros((4, 6), dtype=torch.int8, device=DEV)
+    W1 = torch.zeros((4, 2), dtype=torch.uint8, device=DEV)
+    C = torch.zeros((4, 4), dtype=torch.int32, device=DEV)
+    assert B.call_raw("ternary_gemm_s8", A6.data_ptr(), W1.data_ptr(), C.data_ptr(), 4, 4, 6) == B.ERR_PACK
+    assert B.call_raw("ternary_gemm_s8", A6.data_ptr(), W1.data_ptr(), A6.data_ptr(), 4, 4, 4) == B.ERR_ALIAS
