@@ -109,10 +109,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-rows", type=int, default=4096,
+    ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of the batch the CPU oracle baseline runs on (0: skip)")
     ap.add_argument("--only", choices=["fwd", "dx", "dw"], default=None,
                     help="time a single product instead of the whole step (for profiling)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before timing, run one plain device-to-device copy of this many MiB "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,6 +150,15 @@ def main():
         "dw": lambda: B.ternary_gemm_s8_dw(Ad, dCd, dW=dWd, stream=stream),
     }
     names = [args.only] if args.only else ["fwd", "dx", "dw"]
+
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         for n in names:

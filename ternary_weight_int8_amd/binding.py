@@ -31,6 +31,7 @@ class TgemmPlan(ctypes.Structure):
     _fields_ = [
         ("out_rows", ctypes.c_int64), ("out_cols", ctypes.c_int64), ("contraction", ctypes.c_int64),
         ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
+        ("tiles", ctypes.c_int64),
         ("workgroups", ctypes.c_int64),
         ("threads_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
         ("fast_path", ctypes.c_int32),

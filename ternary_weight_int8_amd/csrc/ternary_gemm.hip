@@ -21,11 +21,14 @@
 // contraction-contiguous rows with an 80-byte pitch, then each wave runs
 // v_mfma_i32_16x16x64_i8 over its sub-tile with int32 accumulators held in
 // registers for the whole contraction.  The 2-bit codes are decoded once per
-// global->LDS tile load, not per MFMA [P10425 "What this adds"].  The next
-// step's global loads are issued before the current step's MFMAs and written
-// to the other LDS buffer after them (two LDS stages, one barrier per step);
-// the pages name this double buffering with a 64-wide step as their next
-// lever [P10425 "What this says"].
+// global->LDS tile load, not per MFMA [P10425 "What this adds"].
+//
+// Pipeline: global loads run PF steps ahead of the MFMAs through a ring of PF
+// register slots; the step after the current one is written from its slot
+// into the other of two LDS buffers once the current step's MFMAs are issued,
+// with one barrier per step.  (The pages' kernel loads synchronously with one
+// stage and names asynchronous double buffering with a 64-wide step as its
+// next lever [P10425 "What this says"].)
 //
 // MFMA operand roles: the P fragment is the instruction's A operand and the Q
 // fragment its B operand, so lane l of a 16x16 result holds O[row l%16][cols
@@ -52,9 +55,21 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int BK = 64;         // contraction per step (one 16x16x64 MFMA)
-constexpr int LP = BK + 16;    // LDS row pitch: 80 B, so 8 consecutive rows
-                               // read at one 16-B column hit 8 distinct
-                               // 16-B bank groups (80*r mod 128 distinct)
+constexpr int LP = BK;         // LDS row pitch (bytes): rows are not padded
+
+// LDS layout of a staged tile: row r holds its four 16-byte contraction
+// chunks in the order chunk c at slot c ^ ((r >> 1) & 3).  Measured on gfx950:
+// with this swizzle both the MFMA fragment reads (16 rows x 4 chunks per
+// wave) and the 4-threads-per-row tile copies run at the full ~220 B/clk/CU
+// ds_read_b128 rate, while an unswizzled or padded (80-byte) pitch halves it.
+__host__ __device__ constexpr int swz(int r, int c) { return r * LP + 16 * (c ^ ((r >> 1) & 3)); }
+
+// Workgroup barrier for LDS only: waits for this wave's LDS operations, not
+// for its outstanding global loads (which __syncthreads() would also drain,
+// defeating the prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Byte c of this word is the int8 weight of code c: 00, 01, FF, 00, i.e.
 // (c & 1) - ((c >> 1) & 1) [P10425 "What this adds"; P10855 PR body].
@@ -125,186 +140,258 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
 }
 
 // ---------------------------------------------------------------------------
-// Stagers.  load() issues the global reads of one step into registers;
-// store() writes them (decoded / transposed) into an LDS tile of BT rows of
-// LP bytes.  Contraction positions >= L are written as 0, so a ragged last
-// step contributes nothing.  Rows beyond the output are clamped to the last
-// valid row (in bounds, computed, never stored).
+// Stagers.  init() fixes a thread's source addresses for the workgroup's
+// tile; load() issues the global reads of the step starting at contraction
+// index c0 into a register slot; store() writes a slot (decoded / transposed)
+// into an LDS tile of BT rows of LP bytes.  `full` is true when the whole step
+// lies inside the contraction; otherwise positions >= L are loaded as 0, so a
+// ragged last step contributes nothing.  Rows beyond the output are clamped to
+// the last valid row (in bounds, computed, never stored).
 // ---------------------------------------------------------------------------
 
-// Rows of an int8 matrix whose rows are contraction-contiguous (A or dC as
-// the Q operand): chunk = 16 bytes, 4 chunks per row per step.
+// Rows of an int8 matrix that run along the contraction (A or dC as the Q
+// operand): 16-byte chunks, 4 per row per step, 4 threads per row; a thread's
+// i-th chunk is in tile row i*64 + tid/4 (the last pass may cover fewer rows).
 template <int BT, bool FAST>
-struct CopyStage {
-  static constexpr int kPer = BT * 4 / kThreads;
-  static_assert(kPer >= 1 && BT * 4 % kThreads == 0, "tile too small");
-  v4i r[kPer];
+struct CopyOp {
+  static constexpr int kPer = (BT + kThreads / 4 - 1) / (kThreads / 4);
+  static_assert(BT % 16 == 0, "tile shape");
+  struct Slot { v4i r[kPer]; };
+  const int8_t *ptr[kPer];
+  int64_t L;
+  int cc, row0;
 
-  __device__ __forceinline__ void load(const int8_t *src, int64_t ld, int64_t nrows,
-                                       int64_t L, int64_t t0, int64_t c0, int tid) {
+  __device__ __forceinline__ static bool has(int i, int row0) {
+    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + row0 < BT;
+  }
+
+  __device__ __forceinline__ void init(const int8_t *src, int64_t ld, int64_t nrows, int64_t L_,
+                                       int64_t t0, int tid) {
+    L = L_;
+    cc = tid & 3;
+    row0 = tid >> 2;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = i * kThreads + tid;
-      const int row = id >> 2, cc = id & 3;
-      const int64_t gr = t0 + row < nrows ? t0 + row : nrows - 1;
-      const int64_t gc = c0 + cc * 16;
-      const int8_t *s = src + gr * ld + gc;
-      if (FAST) {  // L % 16 == 0 and 16-B aligned rows: a chunk is all in or all out
-        r[i] = gc < L ? *reinterpret_cast<const v4i *>(s) : v4i{0, 0, 0, 0};
+      const int64_t row = t0 + i * (kThreads / 4) + row0;
+      ptr[i] = src + (row < nrows ? row : nrows - 1) * ld + cc * 16;
+    }
+  }
+
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    const int64_t gc = c0 + cc * 16;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!has(i, row0)) break;
+      const int8_t *p = ptr[i] + c0;
+      if (FAST && full) {
+        s.r[i] = *reinterpret_cast<const v4i *>(p);
+      } else if (FAST) {  // L % 16 == 0: a chunk is all in or all out
+        // branch-free: read an in-bounds chunk (the row start), keep it only if in
+        const v4i v = *reinterpret_cast<const v4i *>(gc < L ? p : ptr[i]);
+        s.r[i] = gc < L ? v : v4i{0, 0, 0, 0};
       } else {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int b = 0; b < 16; ++b)
-          if (gc + b < L) w[b >> 2] |= (uint32_t)(uint8_t)s[b] << (8 * (b & 3));
-        r[i] = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
+          if (gc + b < L) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
+        s.r[i] = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
       }
     }
   }
 
-  __device__ __forceinline__ void store(int8_t *lds, int tid) const {
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = i * kThreads + tid;
-      *reinterpret_cast<v4i *>(lds + (id >> 2) * LP + (id & 3) * 16) = r[i];
+      if (!has(i, tid >> 2)) break;
+      *reinterpret_cast<v4i *>(lds + swz(i * (kThreads / 4) + (tid >> 2), tid & 3)) = s.r[i];
     }
   }
 };
 
 // Stored ternary weights as the P operand of the forward product: row n of
 // Wpacked holds the codes of column n along K, so a step's 64 codes of a row
-// are 16 contiguous bytes = 4 dwords.  Decoded once here, one 16-B LDS store
-// per dword.
+// are 16 contiguous bytes = 4 dwords, one per thread (4 threads per row, same
+// row assignment as CopyOp).  Decoded once here, one 16-B LDS store per dword.
 template <int BT, bool FAST>
-struct DecodeStage {
-  static constexpr int kPer = BT * 4 / kThreads;
-  static_assert(kPer >= 1 && BT * 4 % kThreads == 0, "tile too small");
-  uint32_t r[kPer];
+struct DecodeOp {
+  static constexpr int kPer = (BT + kThreads / 4 - 1) / (kThreads / 4);
+  static_assert(BT % 16 == 0, "tile shape");
+  struct Slot { uint32_t r[kPer]; };
+  const uint8_t *ptr[kPer];
+  int64_t L;
+  int uc, row0;
 
-  __device__ __forceinline__ void load(const uint8_t *wp, int64_t ld, int64_t nrows,
-                                       int64_t L, int64_t t0, int64_t c0, int tid) {
+  __device__ __forceinline__ static bool has(int i, int row0) {
+    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + row0 < BT;
+  }
+
+  __device__ __forceinline__ void init(const uint8_t *wp, int64_t ld, int64_t nrows, int64_t L_,
+                                       int64_t t0, int tid) {
+    L = L_;
+    uc = tid & 3;
+    row0 = tid >> 2;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = i * kThreads + tid;
-      const int row = id >> 2, uc = id & 3;
-      const int64_t gr = t0 + row < nrows ? t0 + row : nrows - 1;
-      const int64_t gk = c0 + uc * 16;  // first code of this dword
-      const uint8_t *s = wp + gr * ld + (gk >> 2);
-      if (FAST) {  // L % 16 == 0, 4-B aligned rows
-        r[i] = gk < L ? *reinterpret_cast<const uint32_t *>(s) : 0u;
+      const int64_t row = t0 + i * (kThreads / 4) + row0;
+      ptr[i] = wp + (row < nrows ? row : nrows - 1) * ld + uc * 4;
+    }
+  }
+
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    const int64_t gk = c0 + uc * 16;  // first code of this thread's dword
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!has(i, row0)) break;
+      const uint8_t *p = ptr[i] + (c0 >> 2);
+      if (FAST && full) {
+        s.r[i] = *reinterpret_cast<const uint32_t *>(p);
+      } else if (FAST) {  // L % 16 == 0, 4-B aligned rows; branch-free as above
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(gk < L ? p : ptr[i]);
+        s.r[i] = gk < L ? v : 0u;
       } else {
         uint32_t w = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (gk + 4 * b < L) w |= (uint32_t)s[b] << (8 * b);
-        r[i] = w;
+          if (gk + 4 * b < L) w |= (uint32_t)p[b] << (8 * b);
+        s.r[i] = w;
       }
     }
   }
 
-  __device__ __forceinline__ void store(int8_t *lds, int tid) const {
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int id = i * kThreads + tid;
-      *reinterpret_cast<v4i *>(lds + (id >> 2) * LP + (id & 3) * 16) = decode16(r[i]);
+      if (!has(i, tid >> 2)) break;
+      *reinterpret_cast<v4i *>(lds + swz(i * (kThreads / 4) + (tid >> 2), tid & 3)) =
+          decode16(s.r[i]);
     }
   }
 };
 
 // Stored ternary weights as the P operand of dX: LDS row = output column k,
 // contraction along n, but Wpacked rows run along k.  A unit is one packed
-// byte column (4 consecutive k) over 16 consecutive n: 16 byte loads, then for
-// each of the 4 codes of a byte, the 16 weights along n go out as one 16-B LDS
-// store.  Units: (BT/4 byte columns) x (4 groups of 16 n) = BT; threads
-// tid < BT take one each.
+// byte column (4 consecutive k) over 16 consecutive n: 16 byte loads; for each
+// of the 4 codes of a byte, the 16 weights along n go out as one 16-B LDS
+// store.  Units: (BT/4 byte columns) x (4 groups of 16 n) = BT; thread tid < BT
+// takes unit tid.
 template <int BT>
-struct DecodeTStage {
-  static_assert(BT <= kThreads, "tile too large");
-  uint32_t b[16];
+struct DecodeTOp {
+  static_assert(BT <= kThreads && BT % 4 == 0, "tile shape");
+  struct Slot { uint32_t b[16]; };
+  const uint8_t *wp;
+  int64_t ld, L, kbytes, t0;
 
-  __device__ __forceinline__ void load(const uint8_t *wp, int64_t ld, int64_t kbytes,
-                                       int64_t L, int64_t t0, int64_t c0, int tid) {
+  // addresses are formed from the uniform tile origin at each load: cheaper
+  // than carrying per-thread 64-bit row pointers across the loop
+  __device__ __forceinline__ void init(const uint8_t *wp_, int64_t ld_, int64_t kbytes_, int64_t L_,
+                                       int64_t t0_, int tid) {
+    (void)tid;
+    wp = wp_;
+    ld = ld_;
+    kbytes = kbytes_;
+    L = L_;
+    t0 = t0_;
+  }
+
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    (void)full;  // the per-row guard is needed only in the last step; it is cheap
+    const int tid = threadIdx.x;
     if (tid >= BT) return;
     const int bc = tid % (BT / 4), nc = tid / (BT / 4);
-    const int64_t gb = (t0 >> 2) + bc;  // packed byte column (k / 4)
+    const int64_t gb = (t0 >> 2) + bc;
     const bool colok = gb < kbytes;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t n = c0 + nc * 16 + r;
-      b[r] = (colok && n < L) ? (uint32_t)wp[n * ld + gb] : 0u;
+      s.b[r] = (colok && n < L) ? (uint32_t)wp[n * ld + gb] : 0u;
     }
   }
 
-  __device__ __forceinline__ void store(int8_t *lds, int tid) const {
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
     if (tid >= BT) return;
     const int bc = tid % (BT / 4), nc = tid / (BT / 4);
     uint32_t x[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      x[g] = b[4 * g] | (b[4 * g + 1] << 8) | (b[4 * g + 2] << 16) | (b[4 * g + 3] << 24);
+      x[g] = s.b[4 * g] | (s.b[4 * g + 1] << 8) | (s.b[4 * g + 2] << 16) | (s.b[4 * g + 3] << 24);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // code j of each byte = column k = 4*bc + j
       v4i w;
 #pragma unroll
       for (int g = 0; g < 4; ++g) w[g] = (int32_t)weights4((x[g] >> (2 * j)) & 0x03030303u);
-      *reinterpret_cast<v4i *>(lds + (4 * bc + j) * LP + nc * 16) = w;
+      *reinterpret_cast<v4i *>(lds + swz(4 * bc + j, nc)) = w;
     }
   }
 };
 
-// An int8 matrix whose rows run along the contraction index's *other* side
-// (A[m][k] and dC[m][n] for dW): LDS row = output index o, contraction m.  A
-// unit is 4 consecutive o over 16 consecutive m: 16 dword loads (or guarded
-// bytes), 4x4 byte transposes, then 4 16-B LDS stores.  Units: (BT/4) x 4 =
-// BT; threads tid < BT take one each.
+// An int8 matrix whose rows are indexed by the contraction (A[m][k] and
+// dC[m][n] for dW): LDS row = output index o, contraction m.  A unit is 4
+// consecutive o over 16 consecutive m: 16 dword loads (or guarded bytes), 4x4
+// byte transposes, then 4 16-B LDS stores.  Units: (BT/4) x 4 = BT; thread
+// tid < BT takes unit tid.
 template <int BT, bool FAST>
-struct TCopyStage {
-  static_assert(BT <= kThreads, "tile too large");
-  uint32_t r[16];
+struct TCopyOp {
+  static_assert(BT <= kThreads && BT % 4 == 0, "tile shape");
+  struct Slot { uint32_t r[16]; };
+  const int8_t *ptr;
+  int64_t ld, L, m0, o, nout;
+  bool active;
 
-  __device__ __forceinline__ void load(const int8_t *src, int64_t ld, int64_t nout,
-                                       int64_t L, int64_t t0, int64_t c0, int tid) {
-    if (tid >= BT) return;
+  __device__ __forceinline__ void init(const int8_t *src, int64_t ld_, int64_t nout_, int64_t L_,
+                                       int64_t t0, int tid) {
+    ld = ld_;
+    L = L_;
+    nout = nout_;
     const int oq = tid % (BT / 4), mc = tid / (BT / 4);
-    const int64_t o = t0 + 4 * oq;
+    o = t0 + 4 * oq;
+    m0 = mc * 16;
+    active = tid < BT && o < nout;
+    ptr = src + m0 * ld + (active ? o : 0);
+  }
+
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    const int8_t *p = ptr + c0 * ld;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int64_t m = c0 + mc * 16 + i;
-      const int8_t *s = src + m * ld + o;
-      if (FAST) {  // nout % 4 == 0, 4-B aligned rows
-        r[i] = (m < L && o < nout) ? *reinterpret_cast<const uint32_t *>(s) : 0u;
+      const bool in = active && (full || c0 + m0 + i < L);
+      if (FAST) {  // nout % 4 == 0, 4-B aligned rows: the dword is all in or all out
+        s.r[i] = in ? *reinterpret_cast<const uint32_t *>(p + i * ld) : 0u;
       } else {
         uint32_t w = 0;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
-          if (m < L && o + bb < nout) w |= (uint32_t)(uint8_t)s[bb] << (8 * bb);
-        r[i] = w;
+        for (int b = 0; b < 4; ++b)
+          if (in && o + b < nout) w |= (uint32_t)(uint8_t)p[i * ld + b] << (8 * b);
+        s.r[i] = w;
       }
     }
   }
 
-  __device__ __forceinline__ void store(int8_t *lds, int tid) const {
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
     if (tid >= BT) return;
     const int oq = tid % (BT / 4), mc = tid / (BT / 4);
     uint32_t t[4][4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) transpose4x4(&r[4 * g], t[g]);
+    for (int g = 0; g < 4; ++g) transpose4x4(&s.r[4 * g], t[g]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const v4i w{(int32_t)t[0][j], (int32_t)t[1][j], (int32_t)t[2][j], (int32_t)t[3][j]};
-      *reinterpret_cast<v4i *>(lds + (4 * oq + j) * LP + mc * 16) = w;
+      *reinterpret_cast<v4i *>(lds + swz(4 * oq + j, mc)) = w;
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// Tile shapes: BM x BN outputs per workgroup, 2 x 2 waves.
+// Tile shapes: BM x BN outputs per workgroup, WM x WN waves, each wave a
+// (BM/WM) x (BN/WN) block of 16x16 MFMA results; PF = steps of global-load
+// prefetch (register slots); OCC = waves per SIMD the registers are sized for.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WM_, int WN_, int PF_, int OCC_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WM = 2, WN = 2;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_, OCC = OCC_;
+  static_assert(WM * WN * 64 == kThreads, "4 waves");
   static constexpr int TM = BM / WM, TN = BN / WN;  // per wave
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 blocks per wave
+  static_assert(FM * 16 == TM && FN * 16 == TN, "wave tile must be a multiple of 16");
   static constexpr int kLds = 2 * (BM + BN) * LP;
 };
 
@@ -313,36 +400,107 @@ struct Stages;
 
 template <class T, bool FAST>
 struct Stages<FWD, T, FAST> {
-  CopyStage<T::BM, FAST> q;
-  DecodeStage<T::BN, FAST> p;
-  __device__ __forceinline__ void load(const Args &a, int64_t q0, int64_t p0, int64_t c0, int tid) {
-    q.load(a.q, a.ldq, a.R, a.L, q0, c0, tid);
-    p.load(static_cast<const uint8_t *>(a.p), a.ldp, a.Cc, a.L, p0, c0, tid);
+  CopyOp<T::BM, FAST> q;
+  DecodeOp<T::BN, FAST> p;
+  struct Slot {
+    typename CopyOp<T::BM, FAST>::Slot q;
+    typename DecodeOp<T::BN, FAST>::Slot p;
+  };
+  __device__ __forceinline__ void init(const Args &a, int64_t q0, int64_t p0, int tid) {
+    q.init(a.q, a.ldq, a.R, a.L, q0, tid);
+    p.init(static_cast<const uint8_t *>(a.p), a.ldp, a.Cc, a.L, p0, tid);
+  }
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    q.load(s.q, c0, full);
+    p.load(s.p, c0, full);
+  }
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lq, int8_t *lp, int tid) {
+    CopyOp<T::BM, FAST>::store(s.q, lq, tid);
+    DecodeOp<T::BN, FAST>::store(s.p, lp, tid);
   }
 };
 
 template <class T, bool FAST>
 struct Stages<DX, T, FAST> {
-  CopyStage<T::BM, FAST> q;
-  DecodeTStage<T::BN> p;
-  __device__ __forceinline__ void load(const Args &a, int64_t q0, int64_t p0, int64_t c0, int tid) {
-    q.load(a.q, a.ldq, a.R, a.L, q0, c0, tid);
-    p.load(static_cast<const uint8_t *>(a.p), a.ldp, a.Cc >> 2, a.L, p0, c0, tid);
+  CopyOp<T::BM, FAST> q;
+  DecodeTOp<T::BN> p;
+  struct Slot {
+    typename CopyOp<T::BM, FAST>::Slot q;
+    typename DecodeTOp<T::BN>::Slot p;
+  };
+  __device__ __forceinline__ void init(const Args &a, int64_t q0, int64_t p0, int tid) {
+    q.init(a.q, a.ldq, a.R, a.L, q0, tid);
+    p.init(static_cast<const uint8_t *>(a.p), a.ldp, a.Cc >> 2, a.L, p0, tid);
+  }
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    q.load(s.q, c0, full);
+    p.load(s.p, c0, full);
+  }
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lq, int8_t *lp, int tid) {
+    CopyOp<T::BM, FAST>::store(s.q, lq, tid);
+    DecodeTOp<T::BN>::store(s.p, lp, tid);
   }
 };
 
 template <class T, bool FAST>
 struct Stages<DW, T, FAST> {
-  TCopyStage<T::BM, FAST> q;
-  TCopyStage<T::BN, FAST> p;
-  __device__ __forceinline__ void load(const Args &a, int64_t q0, int64_t p0, int64_t c0, int tid) {
-    q.load(a.q, a.ldq, a.R, a.L, q0, c0, tid);
-    p.load(static_cast<const int8_t *>(a.p), a.ldp, a.Cc, a.L, p0, c0, tid);
+  TCopyOp<T::BM, FAST> q;
+  TCopyOp<T::BN, FAST> p;
+  struct Slot {
+    typename TCopyOp<T::BM, FAST>::Slot q;
+    typename TCopyOp<T::BN, FAST>::Slot p;
+  };
+  __device__ __forceinline__ void init(const Args &a, int64_t q0, int64_t p0, int tid) {
+    q.init(a.q, a.ldq, a.R, a.L, q0, tid);
+    p.init(static_cast<const int8_t *>(a.p), a.ldp, a.Cc, a.L, p0, tid);
+  }
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+    q.load(s.q, c0, full);
+    p.load(s.p, c0, full);
+  }
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lq, int8_t *lp, int tid) {
+    TCopyOp<T::BM, FAST>::store(s.q, lq, tid);
+    TCopyOp<T::BN, FAST>::store(s.p, lp, tid);
   }
 };
 
+// One contraction step of a wave's sub-tile: fragments from LDS, FM x FN MFMAs.
+template <class T>
+__device__ __forceinline__ void mfma_step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
+                                          const int8_t *pb) {
+  v4i fp[T::FN];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) fp[j] = *reinterpret_cast<const v4i *>(pb + j * 16 * LP);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const v4i fq = *reinterpret_cast<const v4i *>(qb + i * 16 * LP);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fp[j], fq, acc[i][j], 0, 0, 0);
+  }
+}
+
+// Store one 16x16 result block (this lane's 4 consecutive int32) at (row, col).
+__device__ __forceinline__ void store_block(const Args &a, const v4i &v, int64_t row, int64_t col,
+                                            bool interior) {
+  if (interior) {
+    *reinterpret_cast<v4i *>(a.out + row * a.Cc + col) = v;
+    return;
+  }
+  if (row >= a.R) return;
+  int32_t *o = a.out + row * a.Cc;
+  if (a.vec_out && col + 3 < a.Cc) {
+    *reinterpret_cast<v4i *>(o + col) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < a.Cc) o[col + e] = v[e];
+  }
+}
+
 template <int OP, class T, bool FAST>
-__global__ __launch_bounds__(kThreads) void tgemm_kernel(Args a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(T::OCC)))
+void tgemm_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) int8_t smem[T::kLds];
   int8_t *const sq = smem;                    // [2][BM][LP]
   int8_t *const sp = smem + 2 * T::BM * LP;   // [2][BN][LP]
@@ -361,47 +519,55 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  Stages<OP, T, FAST> st;
-  const int32_t nk = (int32_t)((a.L + BK - 1) / BK);
+  typedef Stages<OP, T, FAST> S;
+  S st;
+  st.init(a, q0, p0, tid);
+  typename S::Slot slot[T::PF];
 
-  st.load(a, q0, p0, 0, tid);
-  st.q.store(sq, tid);
-  st.p.store(sp, tid);
-  __syncthreads();
+  const int32_t nk = (int32_t)((a.L + BK - 1) / BK);  // steps
+  const int32_t nfull = (int32_t)(a.L / BK);          // steps entirely inside L
+  // The loop runs whole groups of PF steps.  Steps past the contraction load
+  // zeros (their loads are guarded off), so padding the last group adds
+  // nothing to the sums and the loop has no early exit.
+  const int32_t ngroups = (nk + T::PF - 1) / T::PF;
 
-  // fragment addresses: row (lane % 16) of each 16-row block, 16-B chunk lane / 16
-  const int frag = (lane & 15) * LP + (lane >> 4) * 16;
+#pragma unroll
+  for (int s = 0; s < T::PF; ++s) st.load(slot[s], (int64_t)s * BK, s < nfull);
+  S::store(slot[0], sq, sp, tid);
+  lds_barrier();
+
+  // fragment addresses: row (lane % 16) of each 16-row block, chunk lane / 16;
+  // block bases are multiples of 16 rows, so the swizzle depends on the lane only
+  const int frag = swz(lane & 15, lane >> 4);
   const int qoff = wm * T::TM * LP + frag;
   const int poff = wn * T::TN * LP + frag;
 
-  for (int32_t kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) st.load(a, q0, p0, (int64_t)(kt + 1) * BK, tid);
-
-    const int8_t *qb = sq + cur * T::BM * LP + qoff;
-    const int8_t *pb = sp + cur * T::BN * LP + poff;
-    v4i fq[T::FM], fp[T::FN];
+  for (int32_t g = 0; g < ngroups; ++g) {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) fq[i] = *reinterpret_cast<const v4i *>(qb + i * 16 * LP);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) fp[j] = *reinterpret_cast<const v4i *>(pb + j * 16 * LP);
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fp[j], fq[i], acc[i][j], 0, 0, 0);
-
-    if (more) {
-      st.q.store(sq + (cur ^ 1) * T::BM * LP, tid);
-      st.p.store(sp + (cur ^ 1) * T::BN * LP, tid);
+    for (int u = 0; u < T::PF; ++u) {
+      const int32_t j = g * T::PF + u;
+      // refill the slot this step's data came from with step j + PF
+      st.load(slot[u], (int64_t)(j + T::PF) * BK, j + T::PF < nfull);
+      const int cur = j & 1;
+      mfma_step<T>(acc, sq + cur * T::BM * LP + qoff, sp + cur * T::BN * LP + poff);
+      S::store(slot[(u + 1) % T::PF], sq + (cur ^ 1) * T::BM * LP, sp + (cur ^ 1) * T::BN * LP,
+               tid);
+      lds_barrier();
     }
-    __syncthreads();
   }
 
   // epilogue: lane holds O[row][col .. col+3] of each 16x16 block
   const int64_t rbase = q0 + wm * T::TM + (lane & 15);
   const int64_t cbase = p0 + wn * T::TN + (lane >> 4) * 4;
+  if (a.vec_out && q0 + T::BM <= a.R && p0 + T::BN <= a.Cc) {  // interior tile
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      int32_t *orow = a.out + (rbase + i * 16) * a.Cc + cbase;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) *reinterpret_cast<v4i *>(orow + j * 16) = acc[i][j];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     const int64_t row = rbase + i * 16;
@@ -425,11 +591,45 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(Args a) {
 // Host side: validation, planning, launch.
 // ---------------------------------------------------------------------------
 
-typedef Tile<256, 128> TileL;
-typedef Tile<128, 128> TileM;
-typedef Tile<64, 64> TileS;
+// Tile shapes per product.  Prefetch depth and occupancy are chosen per
+// product so that no instantiation spills registers: the dX and dW stagers
+// hold 16 registers per slot where the forward's hold 4-6.
+template <int OP>
+struct Tiles;
+template <>
+struct Tiles<FWD> {
+  typedef Tile<256, 128, 2, 2, 2, 2> L;  // large outputs
+  typedef Tile<128, 144, 4, 1, 2, 2> W;  // outputs of ~240 tiles of this size
+  typedef Tile<64, 64, 2, 2, 2, 4> S;    // small / ragged
+};
+template <>
+struct Tiles<DX> {
+  typedef Tile<256, 128, 2, 2, 1, 2> L;
+  typedef Tile<128, 144, 4, 1, 1, 2> W;
+  typedef Tile<64, 64, 2, 2, 2, 2> S;
+};
+template <>
+struct Tiles<DW> {
+  typedef Tile<256, 128, 2, 2, 2, 1> L;
+  typedef Tile<128, 144, 4, 1, 2, 1> W;
+  typedef Tile<64, 64, 2, 2, 2, 2> S;
+};
+typedef Tiles<FWD> TileShapes;  // the shapes (not the tuning) are common
 
-enum TileId { TL = 0, TM_ = 1, TS = 2 };
+enum TileId { TL = 0, TW = 1, TS = 2, kTiles = 3 };
+
+struct TileInfo {
+  int bm, bn, lds;
+  double eff;  // relative MFMA efficiency (operand bytes per MAC read from LDS)
+};
+
+const TileInfo kTileInfo[kTiles] = {
+    // efficiencies relative to the large tile, from measured MI355X runs
+    // (operand bytes staged per MAC grow as the tile shrinks)
+    {TileShapes::L::BM, TileShapes::L::BN, TileShapes::L::kLds, 1.0},
+    {TileShapes::W::BM, TileShapes::W::BN, TileShapes::W::kLds, 0.8},
+    {TileShapes::S::BM, TileShapes::S::BN, TileShapes::S::kLds, 0.3},
+};
 
 struct Shape {
   int64_t R, Cc, L;
@@ -443,23 +643,22 @@ Shape shape_of(int op, int64_t M, int64_t N, int64_t K) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-void tile_dims(int t, int *bm, int *bn) {
-  if (t == TL) { *bm = TileL::BM; *bn = TileL::BN; }
-  else if (t == TM_) { *bm = TileM::BM; *bn = TileM::BN; }
-  else { *bm = TileS::BM; *bn = TileS::BN; }
-}
-
-// Largest tile that still gives every CU (256 of them) work: big tiles read
-// fewer operand bytes per MAC from LDS; small ones fill the chip on small
-// outputs.
+// Pick the tile with the least estimated time: rounds of one workgroup per
+// CU (256 CUs) times the MACs of one tile at that tile's efficiency.
 int pick_tile(const Shape &s) {
   const int64_t cus = 256;
-  for (int t = TL; t <= TS; ++t) {
-    int bm, bn;
-    tile_dims(t, &bm, &bn);
-    if (ceil_div(s.R, bm) * ceil_div(s.Cc, bn) >= 2 * cus) return t;
+  int best = TS;
+  double best_cost = 0;
+  for (int t = 0; t < kTiles; ++t) {
+    const TileInfo &ti = kTileInfo[t];
+    const int64_t tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
+    const double cost = (double)ceil_div(tiles, cus) * ti.bm * ti.bn / ti.eff;
+    if (t == 0 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
   }
-  return TS;
+  return best;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -480,8 +679,8 @@ int check_dims(int op, int64_t M, int64_t N, int64_t K) {
   if (op < FWD || op > DW) return TGEMM_ERR_DIM;
   if (M < 1 || N < 1 || K < 1) return TGEMM_ERR_DIM;
   int64_t t;
-  if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return TGEMM_ERR_DIM;
-  if (!mul_ok(M, N, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, K, &t) || !mul_ok(t, 4, &t) ||
+  // every operand and output byte count (int32 outputs: 4 bytes) fits int64
+  if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
       !mul_ok(K, N, &t) || !mul_ok(t, 4, &t))
     return TGEMM_ERR_DIM;
   if (op != DW && K % 4 != 0) return TGEMM_ERR_PACK;
@@ -489,7 +688,8 @@ int check_dims(int op, int64_t M, int64_t N, int64_t K) {
   const int64_t bound = op == DW ? TGEMM_INT8_MAX_CONTRACTION : TGEMM_TERNARY_MAX_CONTRACTION;
   if (s.L > bound) return TGEMM_ERR_BOUND;
   // smallest tile must keep the workgroup count within a 1-D grid
-  if (ceil_div(s.R, TileS::BM) * ceil_div(s.Cc, TileS::BN) > INT32_MAX) return TGEMM_ERR_DIM;
+  if (ceil_div(s.R, TileShapes::S::BM) * ceil_div(s.Cc, TileShapes::S::BN) > INT32_MAX)
+    return TGEMM_ERR_DIM;
   return TGEMM_OK;
 }
 
@@ -518,9 +718,11 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 
 template <int OP>
 hipError_t launch_op(const Args &a, int tile, bool fast, hipStream_t stream) {
-  if (tile == TL) return launch_f<OP, TileL>(a, fast, stream);
-  if (tile == TM_) return launch_f<OP, TileM>(a, fast, stream);
-  return launch_f<OP, TileS>(a, fast, stream);
+  switch (tile) {
+    case TL: return launch_f<OP, typename Tiles<OP>::L>(a, fast, stream);
+    case TW: return launch_f<OP, typename Tiles<OP>::W>(a, fast, stream);
+    default: return launch_f<OP, typename Tiles<OP>::S>(a, fast, stream);
+  }
 }
 
 int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t N, int64_t K,
@@ -536,8 +738,7 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   if (overlaps(out, obytes, q, qbytes) || overlaps(out, obytes, p, pbytes)) return TGEMM_ERR_ALIAS;
 
   const int tile = pick_tile(s);
-  int bm, bn;
-  tile_dims(tile, &bm, &bn);
+  const TileInfo &ti = kTileInfo[tile];
   Args a;
   a.q = q;
   a.p = p;
@@ -547,15 +748,18 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.L = s.L;
   a.ldq = op == DX ? N : K;
   a.ldp = op == DW ? N : K / 4;
-  a.tiles_c = (int32_t)ceil_div(s.Cc, bn);
-  a.tiles = (int32_t)(ceil_div(s.R, bm) * a.tiles_c);
+  a.tiles_c = (int32_t)ceil_div(s.Cc, ti.bn);
+  a.tiles = (int32_t)(ceil_div(s.R, ti.bm) * a.tiles_c);
   a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
   hipError_t e;
-  if (op == FWD) e = launch_op<FWD>(a, tile, fast, stream);
-  else if (op == DX) e = launch_op<DX>(a, tile, fast, stream);
-  else e = launch_op<DW>(a, tile, fast, stream);
+  if (op == FWD)
+    e = launch_op<FWD>(a, tile, fast, stream);
+  else if (op == DX)
+    e = launch_op<DX>(a, tile, fast, stream);
+  else
+    e = launch_op<DW>(a, tile, fast, stream);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
 
@@ -599,18 +803,17 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
-  const int tile = pick_tile(s);
-  int bm, bn;
-  tile_dims(tile, &bm, &bn);
+  const TileInfo &ti = kTileInfo[pick_tile(s)];
   memset(plan, 0, sizeof(*plan));
   plan->out_rows = s.R;
   plan->out_cols = s.Cc;
   plan->contraction = s.L;
-  plan->tile_rows = bm;
-  plan->tile_cols = bn;
-  plan->workgroups = ceil_div(s.R, bm) * ceil_div(s.Cc, bn);
+  plan->tile_rows = ti.bm;
+  plan->tile_cols = ti.bn;
+  plan->tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
+  plan->workgroups = plan->tiles;
   plan->threads_per_workgroup = kThreads;
-  plan->lds_bytes = 2 * (bm + bn) * LP;
+  plan->lds_bytes = ti.lds;
   const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   return TGEMM_OK;
@@ -619,9 +822,9 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
 int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block, int64_t *row0,
                                int64_t *col0) {
   if (!plan || !row0 || !col0) return TGEMM_ERR_NULL;
-  if (block < 0 || block >= plan->workgroups || plan->workgroups > INT32_MAX) return TGEMM_ERR_DIM;
+  if (block < 0 || block >= plan->workgroups || plan->tiles > INT32_MAX) return TGEMM_ERR_DIM;
   const int64_t tiles_c = ceil_div(plan->out_cols, plan->tile_cols);
-  const int32_t t = xcd_tile((int32_t)block, (int32_t)plan->workgroups);
+  const int32_t t = xcd_tile((int32_t)block, (int32_t)plan->tiles);
   *row0 = (int64_t)(t / tiles_c) * plan->tile_rows;
   *col0 = (int64_t)(t % tiles_c) * plan->tile_cols;
   return TGEMM_OK;

@@ -10,6 +10,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
+from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES, TILES
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -109,11 +110,25 @@ def _coverage(op, M, N, K):
 @pytest.mark.parametrize("op,M,N,K", [
     ("fwd", 1, 16, 16), ("fwd", 300, 272, 96), ("fwd", 16384, 3456, 1280),
     ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
+    ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.threads_per_workgroup == 256
     assert pl.lds_bytes <= 160 * 1024
+    assert pl.workgroups == pl.tiles
+
+
+def test_parity_shapes_reach_every_tile_and_path():
+    # the GPU parity shape lists exercise every tile shape on both load paths
+    for op, shapes in (("fwd", FWD_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
+        seen = set()
+        for s in shapes:
+            pl = B.plan(op, *s)
+            seen.add((pl.tile_rows, pl.tile_cols, pl.fast_path))
+        for tile in TILES:
+            for fast in (0, 1):
+                assert (*tile, fast) in seen, (op, tile, fast)
 
 
 def test_block_out_of_range():

@@ -14,6 +14,7 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
+from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -135,28 +136,9 @@ def test_backward_pair(seed):
 # every tile shape x load path, with ragged edges in all three dimensions
 # ---------------------------------------------------------------------------
 
-FWD_SHAPES = [  # (M, N, K): large / medium / small tile, fast (K%16==0) and slow
-    (4100, 3900, 80), (4100, 3900, 84), (2100, 3900, 80), (2100, 3900, 52),
-    (300, 272, 96), (299, 271, 100), (1, 1, 4), (1, 4097, 36), (1000, 1, 64), (65, 65, 68)]
-DX_SHAPES = [  # (M, N, K): contraction N
-    (4100, 80, 3900), (4100, 84, 3900), (2100, 80, 3900), (2100, 36, 3900),
-    (300, 96, 272), (299, 100, 268), (1, 1, 4), (27, 3456, 1280), (1, 4, 4100)]
-DW_SHAPES = [  # (M, N, K): contraction M
-    (80, 3900, 4100), (81, 3901, 4101), (80, 3900, 2100), (19, 3903, 2101),
-    (96, 272, 300), (97, 271, 299), (1, 1, 1), (1782, 5, 7), (27, 3456, 1280)]
-
-
 def tile_of(op, M, N, K):
     pl = B.plan(op, M, N, K)
     return pl.tile_rows, pl.tile_cols, pl.fast_path
-
-
-def test_shape_lists_reach_every_tile_and_path():
-    for op, shapes in (("fwd", FWD_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
-        seen = {tile_of(op, *s) for s in shapes}
-        for tile in ((256, 128), (128, 128), (64, 64)):
-            for fast in (0, 1):
-                assert (*tile, fast) in seen, (op, tile, fast)
 
 
 @pytest.mark.parametrize("M,N,K", FWD_SHAPES)
@@ -208,7 +190,7 @@ def test_misaligned_bases(offset):
                  oracle.dw(A, dC), "dw misaligned")
 
 
-@pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 3900, 80),
+@pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 1900, 80),
                                       ("dx", 299, 100, 268), ("dw", 97, 271, 299)])
 def test_writes_exactly_the_output(op, M, N, K):
     # the output sits between two canary bands inside one buffer, pre-filled
