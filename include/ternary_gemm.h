@@ -111,7 +111,8 @@ const char *ternary_gemm_status_str(int status);
  * Launch plan the library would use for a call, computed on the host without
  * touching the device (for tests and tooling).  op: 0 forward, 1 dX, 2 dW.
  * Fills the output tile (rows x cols of the row-major output per workgroup),
- * the number of tiles and of workgroups (one tile each), the LDS bytes per
+ * the number of tiles and of workgroups (one tile each), the tile columns per
+ * band of the workgroup -> tile order (see ternary_gemm_tile_of_block), the LDS bytes per
  * workgroup and whether the fast (vector-load) path applies given the base
  * alignments passed in `align` (the smallest power-of-two alignment of the
  * input pointers, in bytes).  Returns TGEMM_OK, or the status the real call
@@ -122,6 +123,7 @@ typedef struct tgemm_plan {
     int32_t tile_rows, tile_cols;
     int64_t tiles;
     int64_t workgroups;
+    int32_t band_cols;
     int32_t threads_per_workgroup;
     int32_t lds_bytes;
     int32_t fast_path;
@@ -132,8 +134,9 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align,
 
 /*
  * Output tile handled by workgroup `block` under a plan (host mirror of the
- * kernel's own workgroup -> tile order, which keeps the tiles that share input
- * rows on one of the chip's eight L2 slices).  Writes the tile's first output
+ * kernel's own workgroup -> tile order: each of the chip's eight L2 slices
+ * gets a contiguous run of a tile order that goes row by row inside bands of
+ * band_cols tile columns, so tiles sharing input rows and columns share an L2).  Writes the tile's first output
  * row and column.  Returns TGEMM_OK, or TGEMM_ERR_DIM if block is out of range.
  */
 int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block,

@@ -33,6 +33,7 @@ class TgemmPlan(ctypes.Structure):
         ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
         ("tiles", ctypes.c_int64),
         ("workgroups", ctypes.c_int64),
+        ("band_cols", ctypes.c_int32),
         ("threads_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
         ("fast_path", ctypes.c_int32),
     ]

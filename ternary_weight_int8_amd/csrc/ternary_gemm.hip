@@ -77,6 +77,11 @@ constexpr uint32_t kCodeTable = 0x00FF0100u;
 
 enum Op { FWD = 0, DX = 1, DW = 2 };
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 struct Args {
   const int8_t *q;    // Q source
   const void *p;      // P source (Wpacked for FWD/DX, dC for DW)
@@ -84,21 +89,35 @@ struct Args {
   int64_t R, Cc, L;   // output rows, output cols, contraction length
   int64_t ldq, ldp;   // row strides (bytes) of the Q and P sources
   int32_t tiles_c;    // column tiles
+  int32_t band_cols;  // tile columns per band of the workgroup -> tile order
   int32_t tiles;      // total tiles (= workgroups)
   int32_t vec_out;    // Cc % 4 == 0 and out 16-B aligned: 16-B stores
 };
 
 // ---------------------------------------------------------------------------
 // Workgroup -> tile order.  The hardware hands workgroup ids to the eight
-// XCDs round-robin (id % 8), and each XCD has its own L2.  The remap gives
-// each XCD a contiguous range of tile ids; tile ids run along the output
-// columns first, so the tiles an XCD runs together share the same Q rows and
-// read them from its L2 instead of HBM.  A bijection on [0, tiles).
+// XCDs round-robin (id % 8), and each XCD has its own L2.  xcd_tile gives each
+// XCD a contiguous range of positions in a linear tile order (a bijection on
+// [0, tiles)).  That order runs row by row inside bands of band_cols tile
+// columns, band after band, so the tiles an XCD runs together share input
+// rows, and with several bands an XCD also touches only its band's columns.
+// The host picks the band count that minimises the operand bytes the eight
+// XCDs fetch between them.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int32_t xcd_tile(int32_t wg, int32_t tiles) {
   const int32_t q = tiles / 8, r = tiles % 8;
   const int32_t x = wg % 8, j = wg / 8;
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+__host__ __device__ inline void tile_rc(int32_t pos, int32_t tiles_r, int32_t tiles_c,
+                                        int32_t band_cols, int32_t *tr, int32_t *tc) {
+  const int32_t per_band = tiles_r * band_cols;
+  const int32_t band = pos / per_band, rem = pos % per_band;
+  const int32_t c0 = band * band_cols;
+  const int32_t w = tiles_c - c0 < band_cols ? tiles_c - c0 : band_cols;
+  *tr = rem / w;
+  *tc = c0 + rem % w;
 }
 
 // ---------------------------------------------------------------------------
@@ -127,18 +146,6 @@ __device__ __forceinline__ v4i decode16(uint32_t x) {
   return w;
 }
 
-// 4x4 byte transpose: out[j] byte r = in[r] byte j
-__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
-  const uint32_t a_lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
-  const uint32_t a_hi = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
-  const uint32_t b_lo = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t b_hi = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
-}
-
 // ---------------------------------------------------------------------------
 // Stagers.  init() fixes a thread's source addresses for the workgroup's
 // tile; load() issues the global reads of the step starting at contraction
@@ -161,8 +168,10 @@ struct CopyOp {
   int64_t L;
   int cc, row0;
 
-  __device__ __forceinline__ static bool has(int i, int row0) {
-    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + row0 < BT;
+  // pass i of this thread covers a tile row; `wave` is wave-uniform (rows of
+  // a wave are 16 consecutive ones and BT % 16 == 0), so this is a scalar test
+  __device__ __forceinline__ static bool has(int i, int wave) {
+    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + 16 * wave < BT;
   }
 
   __device__ __forceinline__ void init(const int8_t *src, int64_t ld, int64_t nrows, int64_t L_,
@@ -181,7 +190,9 @@ struct CopyOp {
     const int64_t gc = c0 + cc * 16;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      if (!has(i, row0)) break;
+      // every thread loads every pass (rows past the tile are clamped to valid
+      // rows, never stored), so the number of loads in flight is the same on
+      // every path and the compiler can wait for exactly the ones it needs
       const int8_t *p = ptr[i] + c0;
       if (FAST && full) {
         s.r[i] = *reinterpret_cast<const v4i *>(p);
@@ -193,16 +204,17 @@ struct CopyOp {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int b = 0; b < 16; ++b)
-          if (gc + b < L) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
+          if (full || gc + b < L) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
         s.r[i] = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
       }
     }
   }
 
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      if (!has(i, tid >> 2)) break;
+      if (!has(i, wave)) break;
       *reinterpret_cast<v4i *>(lds + swz(i * (kThreads / 4) + (tid >> 2), tid & 3)) = s.r[i];
     }
   }
@@ -221,8 +233,8 @@ struct DecodeOp {
   int64_t L;
   int uc, row0;
 
-  __device__ __forceinline__ static bool has(int i, int row0) {
-    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + row0 < BT;
+  __device__ __forceinline__ static bool has(int i, int wave) {
+    return BT % (kThreads / 4) == 0 || i * (kThreads / 4) + 16 * wave < BT;
   }
 
   __device__ __forceinline__ void init(const uint8_t *wp, int64_t ld, int64_t nrows, int64_t L_,
@@ -240,8 +252,7 @@ struct DecodeOp {
   __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
     const int64_t gk = c0 + uc * 16;  // first code of this thread's dword
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (!has(i, row0)) break;
+    for (int i = 0; i < kPer; ++i) {  // every pass, as in CopyOp
       const uint8_t *p = ptr[i] + (c0 >> 2);
       if (FAST && full) {
         s.r[i] = *reinterpret_cast<const uint32_t *>(p);
@@ -252,16 +263,17 @@ struct DecodeOp {
         uint32_t w = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (gk + 4 * b < L) w |= (uint32_t)p[b] << (8 * b);
+          if (full || gk + 4 * b < L) w |= (uint32_t)p[b] << (8 * b);
         s.r[i] = w;
       }
     }
   }
 
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      if (!has(i, tid >> 2)) break;
+      if (!has(i, wave)) break;
       *reinterpret_cast<v4i *>(lds + swz(i * (kThreads / 4) + (tid >> 2), tid & 3)) =
           decode16(s.r[i]);
     }
@@ -294,16 +306,17 @@ struct DecodeTOp {
   }
 
   __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
-    (void)full;  // the per-row guard is needed only in the last step; it is cheap
-    const int tid = threadIdx.x;
-    if (tid >= BT) return;
-    const int bc = tid % (BT / 4), nc = tid / (BT / 4);
-    const int64_t gb = (t0 >> 2) + bc;
-    const bool colok = gb < kbytes;
+    // threads past the BT units repeat unit tid % BT (loaded, never stored), so
+    // every path has the same loads in flight
+    const int ut = threadIdx.x % BT;
+    const int bc = ut % (BT / 4), nc = ut / (BT / 4);
+    // byte columns past the output are clamped to the last one (computed,
+    // never stored); rows need a guard only in steps that reach past L
+    const int64_t gb = (t0 >> 2) + bc < kbytes ? (t0 >> 2) + bc : kbytes - 1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t n = c0 + nc * 16 + r;
-      s.b[r] = (colok && n < L) ? (uint32_t)wp[n * ld + gb] : 0u;
+      s.b[r] = (full || n < L) ? (uint32_t)wp[n * ld + gb] : 0u;
     }
   }
 
@@ -325,57 +338,100 @@ struct DecodeTOp {
 };
 
 // An int8 matrix whose rows are indexed by the contraction (A[m][k] and
-// dC[m][n] for dW): LDS row = output index o, contraction m.  A unit is 4
-// consecutive o over 16 consecutive m: 16 dword loads (or guarded bytes), 4x4
-// byte transposes, then 4 16-B LDS stores.  Units: (BT/4) x 4 = BT; thread
-// tid < BT takes unit tid.
+// dC[m][n] for dW), staged as it lies in memory: LDS row = contraction index m
+// (BK rows per step), BT bytes of output index o per row in 16-byte chunks.
+// The MFMA fragments, which need 16 contraction bytes per output index, are
+// read from it with the transposing LDS read (see Frags<DW>).  A unit is one
+// 16-byte chunk; thread tid takes units tid, tid + 256, ...
+//
+// Placement of chunk c of row m: with an odd number of chunks per row the rows
+// are packed (any 16 consecutive rows start in 16 different 16-byte bank
+// groups); with a power of two, chunk c goes to slot c ^ sw(m), sw spreading
+// 16 consecutive rows over all bank groups.  Both the fragment reads (16 rows
+// x one chunk per half-wave) and the unit stores then touch each bank group
+// once per 256 bytes.
+template <int BT>
+struct RowLayout {
+  static constexpr int kChunks = BT / 16;
+  static_assert(BT % 16 == 0 && (BK * kChunks) % 64 == 0 && (kChunks % 2 == 1 || (kChunks & (kChunks - 1)) == 0), "row length");
+  static_assert(kChunks % 2 == 1 || kChunks <= 16, "row length");
+  __host__ __device__ static constexpr int sw(int m) {
+    return kChunks % 2 == 1 ? 0 : (m / (16 / kChunks)) % kChunks;
+  }
+  __host__ __device__ static constexpr int at(int m, int c) { return m * BT + 16 * (c ^ sw(m)); }
+};
+
 template <int BT, bool FAST>
-struct TCopyOp {
-  static_assert(BT <= kThreads && BT % 4 == 0, "tile shape");
-  struct Slot { uint32_t r[16]; };
-  const int8_t *ptr;
-  int64_t ld, L, m0, o, nout;
-  bool active;
+struct RowCopyOp {
+  typedef RowLayout<BT> Lay;
+  static constexpr int kUnits = BK * Lay::kChunks;  // a multiple of 64: whole waves
+  static constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
+  struct Slot { v4i r[kPer]; };
+  const int8_t *base;          // the matrix, row 0 (an always-valid address)
+  const int8_t *ptr[kPer];     // chunk of unit i in contraction row 0
+  int64_t ld, L, nout;
+  int64_t o[kPer];             // first output index of unit i's chunk
+  int m[kPer];                 // contraction row of unit i within a step
+
+  // unit i of a thread exists for whole waves; `wave` is wave-uniform, so the
+  // store test is a scalar branch
+  __device__ __forceinline__ static bool has(int i, int wave) {
+    return kUnits % kThreads == 0 || i * kThreads + wave * 64 < kUnits;
+  }
+  __device__ __forceinline__ static int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  }
 
   __device__ __forceinline__ void init(const int8_t *src, int64_t ld_, int64_t nout_, int64_t L_,
                                        int64_t t0, int tid) {
+    base = src;
     ld = ld_;
     L = L_;
     nout = nout_;
-    const int oq = tid % (BT / 4), mc = tid / (BT / 4);
-    o = t0 + 4 * oq;
-    m0 = mc * 16;
-    active = tid < BT && o < nout;
-    ptr = src + m0 * ld + (active ? o : 0);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      // a thread without a unit in pass i repeats its pass i - 1 unit (loaded,
+      // never stored): every path then has the same loads in flight
+      const int u = i * kThreads + tid < kUnits ? i * kThreads + tid : (i - 1) * kThreads + tid;
+      const int c = u % Lay::kChunks;
+      m[i] = u / Lay::kChunks;
+      o[i] = t0 + 16 * c;
+      // FAST: nout % 16 == 0, so a chunk is all inside the output range or all
+      // outside; outside ones read the last valid chunk (computed, never stored)
+      const int64_t oc = (FAST && o[i] >= nout) ? nout - 16 : o[i];
+      ptr[i] = src + m[i] * ld + oc;
+    }
   }
 
   __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
-    const int8_t *p = ptr + c0 * ld;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = active && (full || c0 + m0 + i < L);
-      if (FAST) {  // nout % 4 == 0, 4-B aligned rows: the dword is all in or all out
-        s.r[i] = in ? *reinterpret_cast<const uint32_t *>(p + i * ld) : 0u;
+    for (int i = 0; i < kPer; ++i) {
+      const int8_t *p = ptr[i] + c0 * ld;
+      if (FAST && full) {
+        s.r[i] = *reinterpret_cast<const v4i *>(p);
+      } else if (FAST) {
+        // branch-free: rows past the contraction read row 0 and are zeroed
+        const bool in = c0 + m[i] < L;
+        const v4i v = *reinterpret_cast<const v4i *>(in ? p : base);
+        s.r[i] = in ? v : v4i{0, 0, 0, 0};
       } else {
-        uint32_t w = 0;
+        const bool in = full || c0 + m[i] < L;
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (in && o + b < nout) w |= (uint32_t)(uint8_t)p[i * ld + b] << (8 * b);
-        s.r[i] = w;
+        for (int b = 0; b < 16; ++b)
+          if (in && o[i] + b < nout) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
+        s.r[i] = v4i{(int32_t)w[0], (int32_t)w[1], (int32_t)w[2], (int32_t)w[3]};
       }
     }
   }
 
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
-    if (tid >= BT) return;
-    const int oq = tid % (BT / 4), mc = tid / (BT / 4);
-    uint32_t t[4][4];
+    const int wave = wave_id();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) transpose4x4(&s.r[4 * g], t[g]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i w{(int32_t)t[0][j], (int32_t)t[1][j], (int32_t)t[2][j], (int32_t)t[3][j]};
-      *reinterpret_cast<v4i *>(lds + swz(4 * oq + j, mc)) = w;
+    for (int i = 0; i < kPer; ++i) {
+      if (!has(i, wave)) break;
+      const int u = i * kThreads + tid;
+      *reinterpret_cast<v4i *>(lds + Lay::at(u / Lay::kChunks, u % Lay::kChunks)) = s.r[i];
     }
   }
 };
@@ -383,11 +439,14 @@ struct TCopyOp {
 // ---------------------------------------------------------------------------
 // Tile shapes: BM x BN outputs per workgroup, WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 16x16 MFMA results; PF = steps of global-load
-// prefetch (register slots); OCC = waves per SIMD the registers are sized for.
+// prefetch (register slots); OCC = waves per SIMD the registers are sized for;
+// PIN = keep each step's global loads ahead of its MFMAs (without it the
+// compiler may sink them below, shortening the prefetch distance).
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_, int PF_, int OCC_>
+template <int BM_, int BN_, int WM_, int WN_, int PF_, int OCC_, bool PIN_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_, OCC = OCC_;
+  static constexpr bool PIN = PIN_;
   static_assert(WM * WN * 64 == kThreads, "4 waves");
   static constexpr int TM = BM / WM, TN = BN / WN;  // per wave
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 blocks per wave
@@ -444,11 +503,11 @@ struct Stages<DX, T, FAST> {
 
 template <class T, bool FAST>
 struct Stages<DW, T, FAST> {
-  TCopyOp<T::BM, FAST> q;
-  TCopyOp<T::BN, FAST> p;
+  RowCopyOp<T::BM, FAST> q;
+  RowCopyOp<T::BN, FAST> p;
   struct Slot {
-    typename TCopyOp<T::BM, FAST>::Slot q;
-    typename TCopyOp<T::BN, FAST>::Slot p;
+    typename RowCopyOp<T::BM, FAST>::Slot q;
+    typename RowCopyOp<T::BN, FAST>::Slot p;
   };
   __device__ __forceinline__ void init(const Args &a, int64_t q0, int64_t p0, int tid) {
     q.init(a.q, a.ldq, a.R, a.L, q0, tid);
@@ -459,26 +518,87 @@ struct Stages<DW, T, FAST> {
     p.load(s.p, c0, full);
   }
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lq, int8_t *lp, int tid) {
-    TCopyOp<T::BM, FAST>::store(s.q, lq, tid);
-    TCopyOp<T::BN, FAST>::store(s.p, lp, tid);
+    RowCopyOp<T::BM, FAST>::store(s.q, lq, tid);
+    RowCopyOp<T::BN, FAST>::store(s.p, lp, tid);
   }
 };
 
-// One contraction step of a wave's sub-tile: fragments from LDS, FM x FN MFMAs.
+// One contraction step of a wave's sub-tile: fragments from LDS, FM x FN
+// MFMAs.  Frags<OP, T> holds the lane's fragment addresses inside one LDS
+// stage; step() reads the fragments of the stage at (qb, pb) and accumulates.
 template <class T>
-__device__ __forceinline__ void mfma_step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
-                                          const int8_t *pb) {
-  v4i fp[T::FN];
+__device__ __forceinline__ void mfma_block(v4i (&acc)[T::FM][T::FN], const v4i (&fp)[T::FN],
+                                           const v4i &fq, int i) {
 #pragma unroll
-  for (int j = 0; j < T::FN; ++j) fp[j] = *reinterpret_cast<const v4i *>(pb + j * 16 * LP);
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    const v4i fq = *reinterpret_cast<const v4i *>(qb + i * 16 * LP);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fp[j], fq, acc[i][j], 0, 0, 0);
-  }
+  for (int j = 0; j < T::FN; ++j)
+    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fp[j], fq, acc[i][j], 0, 0, 0);
 }
+
+// Forward and dX: contraction-contiguous LDS rows (swz layout), one 16-byte
+// read per fragment: row lane % 16 of the 16-row block, chunk lane / 16.
+template <int OP, class T>
+struct Frags {
+  int qoff, poff;
+  __device__ __forceinline__ void init(int lane, int wm, int wn) {
+    // block bases are multiples of 16 rows, so the swizzle depends on the lane only
+    const int frag = swz(lane & 15, lane >> 4);
+    qoff = wm * T::TM * LP + frag;
+    poff = wn * T::TN * LP + frag;
+  }
+  __device__ __forceinline__ void step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
+                                       const int8_t *pb) const {
+    v4i fp[T::FN];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) fp[j] = *reinterpret_cast<const v4i *>(pb + poff + j * 16 * LP);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+      mfma_block<T>(acc, fp, *reinterpret_cast<const v4i *>(qb + qoff + i * 16 * LP), i);
+  }
+};
+
+// dW: LDS rows indexed by the contraction (RowLayout).  ds_read_b64_tr_b8
+// transposes 8x8 bytes inside each 16-lane group: result byte b of lane i is
+// byte i % 8 of the 8 bytes that lane 2b + i / 8 of the group addressed.  So if
+// lanes 2r and 2r + 1 address the two halves of a 16-byte chunk (16 output
+// indices) in contraction row m_r, lane i receives output index i at the 8
+// rows m_0 .. m_7.  Lane group g takes rows 8g + r in the first read and
+// 32 + 8g + r in the second, which fills the 16 contraction bytes of every
+// lane of a fragment; the Q and P fragments use the same rows for the same
+// bytes, so the products pair matching contraction indices.
+template <class T>
+struct Frags<DW, T> {
+  typedef RowLayout<T::BM> QL;
+  typedef RowLayout<T::BN> PL;
+  int qoff[T::FM], poff[T::FN];
+
+  template <class Lay>
+  __device__ __forceinline__ static int off(int c, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int m = 8 * g + (i >> 1);
+    return Lay::at(m, c) + 8 * (i & 1);
+  }
+  __device__ __forceinline__ void init(int lane, int wm, int wn) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) qoff[i] = off<QL>(wm * T::FM + i, lane);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) poff[j] = off<PL>(wn * T::FN + j, lane);
+  }
+  __device__ __forceinline__ static v4i frag(const int8_t *p, int second) {
+    typedef int32_t v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p));
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p + second));
+    return v4i{lo.x, lo.y, hi.x, hi.y};
+  }
+  __device__ __forceinline__ void step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
+                                       const int8_t *pb) const {
+    v4i fp[T::FN];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) fp[j] = frag(pb + poff[j], 32 * T::BN);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) mfma_block<T>(acc, fp, frag(qb + qoff[i], 32 * T::BM), i);
+  }
+};
 
 // Store one 16x16 result block (this lane's 4 consecutive int32) at (row, col).
 __device__ __forceinline__ void store_block(const Args &a, const v4i &v, int64_t row, int64_t col,
@@ -509,9 +629,11 @@ void tgemm_kernel(Args a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
 
-  const int32_t tile = xcd_tile((int32_t)blockIdx.x, a.tiles);
-  const int64_t q0 = (int64_t)(tile / a.tiles_c) * T::BM;
-  const int64_t p0 = (int64_t)(tile % a.tiles_c) * T::BN;
+  int32_t tr, tc;
+  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles), a.tiles / a.tiles_c, a.tiles_c, a.band_cols, &tr,
+          &tc);
+  const int64_t q0 = (int64_t)tr * T::BM;
+  const int64_t p0 = (int64_t)tc * T::BN;
 
   v4i acc[T::FM][T::FN];
 #pragma unroll
@@ -536,25 +658,30 @@ void tgemm_kernel(Args a) {
   S::store(slot[0], sq, sp, tid);
   lds_barrier();
 
-  // fragment addresses: row (lane % 16) of each 16-row block, chunk lane / 16;
-  // block bases are multiples of 16 rows, so the swizzle depends on the lane only
-  const int frag = swz(lane & 15, lane >> 4);
-  const int qoff = wm * T::TM * LP + frag;
-  const int poff = wn * T::TN * LP + frag;
+  Frags<OP, T> fr;
+  fr.init(lane, wm, wn);
 
-  for (int32_t g = 0; g < ngroups; ++g) {
+  // one group of PF steps; `full` says that every step it loads lies inside
+  // the contraction (then the loads carry no guard at all)
+  auto group = [&](int32_t g, auto full) {
 #pragma unroll
     for (int u = 0; u < T::PF; ++u) {
       const int32_t j = g * T::PF + u;
       // refill the slot this step's data came from with step j + PF
-      st.load(slot[u], (int64_t)(j + T::PF) * BK, j + T::PF < nfull);
+      st.load(slot[u], (int64_t)(j + T::PF) * BK, decltype(full)::value || j + T::PF < nfull);
+      if constexpr (T::PIN) __builtin_amdgcn_sched_barrier(0);
       const int cur = j & 1;
-      mfma_step<T>(acc, sq + cur * T::BM * LP + qoff, sp + cur * T::BN * LP + poff);
+      fr.step(acc, sq + cur * T::BM * LP, sp + cur * T::BN * LP);
       S::store(slot[(u + 1) % T::PF], sq + (cur ^ 1) * T::BM * LP, sp + (cur ^ 1) * T::BN * LP,
                tid);
       lds_barrier();
     }
-  }
+  };
+  // groups g whose loads (steps up to (g + 2) * PF - 1) are all full
+  const int32_t gfull = nfull / T::PF - 1 > 0 ? nfull / T::PF - 1 : 0;
+  int32_t g = 0;
+  for (; g < gfull; ++g) group(g, Flag<true>());
+  for (; g < ngroups; ++g) group(g, Flag<false>());
 
   // epilogue: lane holds O[row][col .. col+3] of each 16x16 block
   const int64_t rbase = q0 + wm * T::TM + (lane & 15);
@@ -591,9 +718,11 @@ void tgemm_kernel(Args a) {
 // Host side: validation, planning, launch.
 // ---------------------------------------------------------------------------
 
-// Tile shapes per product.  Prefetch depth and occupancy are chosen per
-// product so that no instantiation spills registers: the dX and dW stagers
-// hold 16 registers per slot where the forward's hold 4-6.
+// Tile shapes per product.  Prefetch depth, occupancy and load pinning are
+// chosen per product from measured MI355X runs, such that no instantiation
+// spills registers (the dX stager holds 32 registers per slot).  At occupancy
+// 2 the dW accumulators stay in VGPRs; at 1 the compiler moves them to AGPRs
+// and copies them between sets every step.
 template <int OP>
 struct Tiles;
 template <>
@@ -604,14 +733,14 @@ struct Tiles<FWD> {
 };
 template <>
 struct Tiles<DX> {
-  typedef Tile<256, 128, 2, 2, 1, 2> L;
-  typedef Tile<128, 144, 4, 1, 1, 2> W;
-  typedef Tile<64, 64, 2, 2, 2, 2> S;
+  typedef Tile<256, 128, 2, 2, 1, 2, true> L;
+  typedef Tile<128, 144, 4, 1, 1, 2, true> W;
+  typedef Tile<64, 64, 2, 2, 2, 2, true> S;
 };
 template <>
 struct Tiles<DW> {
-  typedef Tile<256, 128, 2, 2, 2, 1> L;
-  typedef Tile<128, 144, 4, 1, 2, 1> W;
+  typedef Tile<256, 128, 2, 2, 4, 1> L;
+  typedef Tile<128, 144, 4, 1, 2, 2> W;
   typedef Tile<64, 64, 2, 2, 2, 2> S;
 };
 typedef Tiles<FWD> TileShapes;  // the shapes (not the tuning) are common
@@ -661,6 +790,25 @@ int pick_tile(const Shape &s) {
   return best;
 }
 
+// Bands of tile columns for the workgroup order: with nb bands, each XCD
+// reads about nb/8 of the Q operand (rows) and 1/nb of the P operand
+// (columns); the eight XCDs fetch about nb*Q + 8*P/nb bytes between them.
+int32_t pick_band_cols(int op, int64_t M, int64_t N, int64_t K, int32_t tiles_c) {
+  const double q = op == DX ? (double)M * N : (double)M * K;          // Q operand bytes
+  const double p = op == DW ? (double)M * N : (double)N * (K / 4);    // P operand bytes
+  int best_nb = 1;
+  double best = 0;
+  for (int nb = 1; nb <= 8; nb *= 2) {
+    if (nb > tiles_c) break;
+    const double bytes = nb * q + 8.0 * p / nb;
+    if (nb == 1 || bytes < best) {
+      best = bytes;
+      best_nb = nb;
+    }
+  }
+  return (int32_t)ceil_div(tiles_c, best_nb);
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
@@ -697,7 +845,7 @@ bool fast_ok(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_
   (void)M;
   if (op == FWD) return K % 16 == 0 && qalign % 16 == 0 && palign % 4 == 0;
   if (op == DX) return N % 16 == 0 && qalign % 16 == 0;
-  return K % 4 == 0 && N % 4 == 0 && qalign % 4 == 0 && palign % 4 == 0;
+  return K % 16 == 0 && N % 16 == 0 && qalign % 16 == 0 && palign % 16 == 0;
 }
 
 uintptr_t align_of(const void *p) {
@@ -750,6 +898,7 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.ldp = op == DW ? N : K / 4;
   a.tiles_c = (int32_t)ceil_div(s.Cc, ti.bn);
   a.tiles = (int32_t)(ceil_div(s.R, ti.bm) * a.tiles_c);
+  a.band_cols = pick_band_cols(op, M, N, K, a.tiles_c);
   a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
@@ -812,6 +961,7 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->tile_cols = ti.bn;
   plan->tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
   plan->workgroups = plan->tiles;
+  plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
   plan->threads_per_workgroup = kThreads;
   plan->lds_bytes = ti.lds;
   const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
@@ -823,10 +973,12 @@ int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block, int64_t *r
                                int64_t *col0) {
   if (!plan || !row0 || !col0) return TGEMM_ERR_NULL;
   if (block < 0 || block >= plan->workgroups || plan->tiles > INT32_MAX) return TGEMM_ERR_DIM;
-  const int64_t tiles_c = ceil_div(plan->out_cols, plan->tile_cols);
-  const int32_t t = xcd_tile((int32_t)block, (int32_t)plan->tiles);
-  *row0 = (int64_t)(t / tiles_c) * plan->tile_rows;
-  *col0 = (int64_t)(t % tiles_c) * plan->tile_cols;
+  const int32_t tiles_c = (int32_t)ceil_div(plan->out_cols, plan->tile_cols);
+  int32_t tr, tc;
+  tile_rc(xcd_tile((int32_t)block, (int32_t)plan->tiles), (int32_t)(plan->tiles / tiles_c), tiles_c,
+          plan->band_cols, &tr, &tc);
+  *row0 = (int64_t)tr * plan->tile_rows;
+  *col0 = (int64_t)tc * plan->tile_cols;
   return TGEMM_OK;
 }
 

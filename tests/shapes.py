@@ -16,11 +16,11 @@ DX_SHAPES = [  # contraction N
     (300, 96, 272), (299, 100, 268),
     (1, 1, 4), (27, 3456, 1280), (1, 4, 4100)]
 
-DW_SHAPES = [  # contraction M
-    (80, 3900, 8200), (81, 3901, 8201),
-    (80, 900, 4100), (80, 901, 4101),
-    (80, 3900, 4100), (80, 3901, 4101),
-    (96, 272, 300), (97, 271, 299),
-    (1, 1, 1), (1782, 5, 7), (27, 3456, 1280)]
+DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
+    (80, 3904, 8208), (81, 3901, 8201),
+    (80, 912, 4112), (80, 901, 4101),
+    (80, 3904, 4112), (80, 3901, 4101),
+    (96, 272, 304), (97, 271, 299),
+    (1, 1, 1), (1782, 5, 7), (1782, 16, 16), (27, 3456, 1280)]
 
 TILES = ((256, 128), (128, 144), (64, 64))

@@ -88,6 +88,18 @@ def test_large_full(large_inputs):
     assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), "large seed 1")
 
 
+def test_large_backward_full(large_inputs):
+    # dX and dW at the timed shape, on the same inputs the benchmark draws
+    c = synth.CONFIGS["large"]
+    M, N, K = c["M"], c["N"], c["K"]
+    A, Wp = large_inputs
+    dC = synth.uniform_int8(1, synth.STREAM_DC, M, N)
+    say("large dX 16384x3456x1280 seed=1, every element")
+    assert_exact(gpu_dx(dC, Wp, K), oracle.dx(dC, Wp, K), "large dX")
+    say("large dW 16384x3456x1280 seed=1, every element")
+    assert_exact(gpu_dw(A, dC), oracle.dw(A, dC), "large dW")
+
+
 @pytest.mark.parametrize("seed", [2, 3])
 def test_large_other_seeds(seed):
     # every 7th row plus the last row and every row of the first tile row,
