@@ -11,17 +11,22 @@
 // One kernel template computes all three products.  Every product writes a
 // row-major int32 output O[R][Cc] = sum over a contraction of length L:
 //
-//   product   O      R   Cc  L   Q operand (rows of O)   P operand (cols of O)
-//   forward   C      M   N   K   A[m][.]       copied    W(., n) decoded from Wpacked
-//   dX        dX     M   K   N   dC[m][.]      copied    W(k, .) decoded + transposed
-//   dW        dW     K   N   M   A[.][k]     transposed  dC[.][n]    transposed
+//   product   O      R   Cc  L   Q operand (rows of O)      P operand (cols of O)
+//   forward   C      M   N   K   A[m][.]   contraction-     W(., n) decoded, contraction-
+//                                          contiguous rows  contiguous rows
+//   dX        dX     M   K   N   dC[m][.]  same             Wpacked rows n decoded as they
+//                                                           lie (rows = contraction)
+//   dW        dW     K   N   M   A[.][k]   rows as they     dC[.][n] rows as they lie
+//                                          lie (contraction)
 //
 // A workgroup of 4 waves owns a BM x BN tile of O.  Per step of 64 along the
-// contraction it stages a BM x 64 Q tile and a BN x 64 P tile into LDS as s8,
-// contraction-contiguous rows with an 80-byte pitch, then each wave runs
-// v_mfma_i32_16x16x64_i8 over its sub-tile with int32 accumulators held in
-// registers for the whole contraction.  The 2-bit codes are decoded once per
-// global->LDS tile load, not per MFMA [P10425 "What this adds"].
+// contraction it stages the step's Q and P data into LDS (decoding the 2-bit
+// codes once per global->LDS tile load [P10425 "What this adds"]), then each
+// wave runs v_mfma_i32_16x16x64_i8 over its sub-tile with int32 accumulators
+// held in registers for the whole contraction.  Contraction-contiguous rows
+// are read as fragments with 16-byte LDS reads; rows indexed by the
+// contraction are read with the transposing LDS read (TrRead), which yields
+// the same byte order, so any pairing of the two kinds is valid.
 //
 // Pipeline: global loads run PF steps ahead of the MFMAs through a ring of PF
 // register slots; the step after the current one is written from its slot
@@ -280,63 +285,6 @@ struct DecodeOp {
   }
 };
 
-// Stored ternary weights as the P operand of dX: LDS row = output column k,
-// contraction along n, but Wpacked rows run along k.  A unit is one packed
-// byte column (4 consecutive k) over 16 consecutive n: 16 byte loads; for each
-// of the 4 codes of a byte, the 16 weights along n go out as one 16-B LDS
-// store.  Units: (BT/4 byte columns) x (4 groups of 16 n) = BT; thread tid < BT
-// takes unit tid.
-template <int BT>
-struct DecodeTOp {
-  static_assert(BT <= kThreads && BT % 4 == 0, "tile shape");
-  struct Slot { uint32_t b[16]; };
-  const uint8_t *wp;
-  int64_t ld, L, kbytes, t0;
-
-  // addresses are formed from the uniform tile origin at each load: cheaper
-  // than carrying per-thread 64-bit row pointers across the loop
-  __device__ __forceinline__ void init(const uint8_t *wp_, int64_t ld_, int64_t kbytes_, int64_t L_,
-                                       int64_t t0_, int tid) {
-    (void)tid;
-    wp = wp_;
-    ld = ld_;
-    kbytes = kbytes_;
-    L = L_;
-    t0 = t0_;
-  }
-
-  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
-    // threads past the BT units repeat unit tid % BT (loaded, never stored), so
-    // every path has the same loads in flight
-    const int ut = threadIdx.x % BT;
-    const int bc = ut % (BT / 4), nc = ut / (BT / 4);
-    // byte columns past the output are clamped to the last one (computed,
-    // never stored); rows need a guard only in steps that reach past L
-    const int64_t gb = (t0 >> 2) + bc < kbytes ? (t0 >> 2) + bc : kbytes - 1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t n = c0 + nc * 16 + r;
-      s.b[r] = (full || n < L) ? (uint32_t)wp[n * ld + gb] : 0u;
-    }
-  }
-
-  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
-    if (tid >= BT) return;
-    const int bc = tid % (BT / 4), nc = tid / (BT / 4);
-    uint32_t x[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      x[g] = s.b[4 * g] | (s.b[4 * g + 1] << 8) | (s.b[4 * g + 2] << 16) | (s.b[4 * g + 3] << 24);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // code j of each byte = column k = 4*bc + j
-      v4i w;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) w[g] = (int32_t)weights4((x[g] >> (2 * j)) & 0x03030303u);
-      *reinterpret_cast<v4i *>(lds + swz(4 * bc + j, nc)) = w;
-    }
-  }
-};
-
 // An int8 matrix whose rows are indexed by the contraction (A[m][k] and
 // dC[m][n] for dW), staged as it lies in memory: LDS row = contraction index m
 // (BK rows per step), BT bytes of output index o per row in 16-byte chunks.
@@ -344,21 +292,32 @@ struct DecodeTOp {
 // read from it with the transposing LDS read (see Frags<DW>).  A unit is one
 // 16-byte chunk; thread tid takes units tid, tid + 256, ...
 //
-// Placement of chunk c of row m: with an odd number of chunks per row the rows
-// are packed (any 16 consecutive rows start in 16 different 16-byte bank
-// groups); with a power of two, chunk c goes to slot c ^ sw(m), sw spreading
-// 16 consecutive rows over all bank groups.  Both the fragment reads (16 rows
-// x one chunk per half-wave) and the unit stores then touch each bank group
-// once per 256 bytes.
+// Placement of chunk c of row m (RowLayout).  The fragment reads (Frags)
+// take 16 rows per half-wave, rows {16g + 8h + b} for g in a pair of lane
+// groups and b < 8, all at one chunk c; the unit stores write 16 consecutive
+// units.  With a power-of-two number of chunks per row, chunk c goes to slot
+// c ^ sw(m), sw mapping each such row set onto distinct 16-byte bank groups.
+// With an odd number (144-byte rows: 9), rows are packed and every second
+// block of 16 rows is shifted by 128 bytes, which does the same.  A model of
+// the 64 banks (checked for all four row lengths) and the counters on MI355X
+// both show no conflicts.
 template <int BT>
 struct RowLayout {
   static constexpr int kChunks = BT / 16;
-  static_assert(BT % 16 == 0 && (BK * kChunks) % 64 == 0 && (kChunks % 2 == 1 || (kChunks & (kChunks - 1)) == 0), "row length");
-  static_assert(kChunks % 2 == 1 || kChunks <= 16, "row length");
+  static_assert(BT % 16 == 0 && (BK * kChunks) % 64 == 0, "row length");
+  static_assert(kChunks == 4 || kChunks == 8 || kChunks == 16 || kChunks % 2 == 1, "row length");
+  static constexpr bool kOdd = kChunks % 2 == 1;
   __host__ __device__ static constexpr int sw(int m) {
-    return kChunks % 2 == 1 ? 0 : (m / (16 / kChunks)) % kChunks;
+    return kChunks == 16  ? (m & 7) | (((m >> 4) & 1) << 3)
+           : kChunks == 8 ? ((m >> 1) & 3) | (((m >> 4) & 1) << 2)
+           : kChunks == 4 ? ((m >> 2) & 1) | (((m >> 4) & 1) << 1)
+                          : 0;
   }
-  __host__ __device__ static constexpr int at(int m, int c) { return m * BT + 16 * (c ^ sw(m)); }
+  __host__ __device__ static constexpr int base(int m) {
+    return m * BT + (kOdd ? 128 * (((m >> 4) + 1) >> 1) : 0);
+  }
+  __host__ __device__ static constexpr int at(int m, int c) { return base(m) + 16 * (c ^ sw(m)); }
+  static constexpr int kBytes = BK * BT + (kOdd ? 256 : 0);  // one stage
 };
 
 template <int BT, bool FAST>
@@ -436,6 +395,78 @@ struct RowCopyOp {
   }
 };
 
+// Stored ternary weights as the P operand of dX, staged as they lie: Wpacked
+// row n holds the codes of contraction index n along the output index k, so
+// LDS row = n and one packed dword (16 codes, k .. k + 15) decodes into one
+// 16-byte chunk of that row.  Layout, units and clamping as RowCopyOp; the
+// fragments are read transposed (Frags<DX>).
+template <int BT, bool FAST>
+struct DecodeRowOp {
+  typedef RowLayout<BT> Lay;
+  static constexpr int kUnits = BK * Lay::kChunks;
+  static constexpr int kPer = (kUnits + kThreads - 1) / kThreads;
+  struct Slot { uint32_t r[kPer]; };
+  const uint8_t *base;         // Wpacked, row 0 (an always-valid address)
+  const uint8_t *ptr[kPer];    // unit i's dword in contraction row 0
+  int64_t ld, L, kbytes;       // row stride, contraction length, packed bytes per row
+  int64_t gb[kPer];            // first packed byte of unit i's dword
+  int m[kPer];                 // contraction row of unit i within a step
+
+  __device__ __forceinline__ static bool has(int i, int wave) {
+    return kUnits % kThreads == 0 || i * kThreads + wave * 64 < kUnits;
+  }
+
+  __device__ __forceinline__ void init(const uint8_t *wp, int64_t ld_, int64_t kbytes_, int64_t L_,
+                                       int64_t t0, int tid) {
+    base = wp;
+    ld = ld_;
+    L = L_;
+    kbytes = kbytes_;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = i * kThreads + tid < kUnits ? i * kThreads + tid : (i - 1) * kThreads + tid;
+      const int c = u % Lay::kChunks;
+      m[i] = u / Lay::kChunks;
+      gb[i] = (t0 >> 2) + 4 * c;
+      // FAST: kbytes % 4 == 0, so a dword is all inside the row or all outside;
+      // outside ones read the last valid dword (computed, never stored)
+      const int64_t gbc = (FAST && gb[i] >= kbytes) ? kbytes - 4 : gb[i];
+      ptr[i] = wp + m[i] * ld + gbc;
+    }
+  }
+
+  __device__ __forceinline__ void load(Slot &s, int64_t c0, bool full) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint8_t *p = ptr[i] + c0 * ld;
+      if (FAST && full) {
+        s.r[i] = *reinterpret_cast<const uint32_t *>(p);
+      } else if (FAST) {
+        const bool in = c0 + m[i] < L;
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(in ? p : base);
+        s.r[i] = in ? v : 0u;
+      } else {
+        const bool in = full || c0 + m[i] < L;
+        uint32_t w = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (in && gb[i] + b < kbytes) w |= (uint32_t)p[b] << (8 * b);
+        s.r[i] = w;
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!has(i, wave)) break;
+      const int u = i * kThreads + tid;
+      *reinterpret_cast<v4i *>(lds + Lay::at(u / Lay::kChunks, u % Lay::kChunks)) = decode16(s.r[i]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tile shapes: BM x BN outputs per workgroup, WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 16x16 MFMA results; PF = steps of global-load
@@ -451,7 +482,6 @@ struct Tile {
   static constexpr int TM = BM / WM, TN = BN / WN;  // per wave
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 blocks per wave
   static_assert(FM * 16 == TM && FN * 16 == TN, "wave tile must be a multiple of 16");
-  static constexpr int kLds = 2 * (BM + BN) * LP;
 };
 
 template <int OP, class T, bool FAST>
@@ -482,10 +512,10 @@ struct Stages<FWD, T, FAST> {
 template <class T, bool FAST>
 struct Stages<DX, T, FAST> {
   CopyOp<T::BM, FAST> q;
-  DecodeTOp<T::BN> p;
+  DecodeRowOp<T::BN, FAST> p;
   struct Slot {
     typename CopyOp<T::BM, FAST>::Slot q;
-    typename DecodeTOp<T::BN>::Slot p;
+    typename DecodeRowOp<T::BN, FAST>::Slot p;
   };
   __device__ __forceinline__ void init(const Args &a, int64_t q0, int64_t p0, int tid) {
     q.init(a.q, a.ldq, a.R, a.L, q0, tid);
@@ -497,7 +527,7 @@ struct Stages<DX, T, FAST> {
   }
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lq, int8_t *lp, int tid) {
     CopyOp<T::BM, FAST>::store(s.q, lq, tid);
-    DecodeTOp<T::BN>::store(s.p, lp, tid);
+    DecodeRowOp<T::BN, FAST>::store(s.p, lp, tid);
   }
 };
 
@@ -556,33 +586,23 @@ struct Frags {
   }
 };
 
-// dW: LDS rows indexed by the contraction (RowLayout).  ds_read_b64_tr_b8
-// transposes 8x8 bytes inside each 16-lane group: result byte b of lane i is
-// byte i % 8 of the 8 bytes that lane 2b + i / 8 of the group addressed.  So if
-// lanes 2r and 2r + 1 address the two halves of a 16-byte chunk (16 output
-// indices) in contraction row m_r, lane i receives output index i at the 8
-// rows m_0 .. m_7.  Lane group g takes rows 8g + r in the first read and
-// 32 + 8g + r in the second, which fills the 16 contraction bytes of every
-// lane of a fragment; the Q and P fragments use the same rows for the same
-// bytes, so the products pair matching contraction indices.
-template <class T>
-struct Frags<DW, T> {
-  typedef RowLayout<T::BM> QL;
-  typedef RowLayout<T::BN> PL;
-  int qoff[T::FM], poff[T::FN];
-
+// Transposing fragment reads from a RowLayout tile (rows = contraction).
+// ds_read_b64_tr_b8 transposes 8x8 bytes inside each 16-lane group: result
+// byte b of lane i is byte i % 8 of the 8 bytes that lane 2b + i / 8 of the
+// group addressed.  So if lanes 2r and 2r + 1 address the two halves of a
+// 16-byte chunk (16 output indices) in contraction row m_r, lane i receives
+// output index i at the 8 rows m_0 .. m_7.  Lane group g takes rows
+// 16g .. 16g + 7 in the first read and 16g + 8 .. 16g + 15 in the second, so
+// byte p of lane group g holds contraction index 16g + p: the same order as a
+// 16-byte read of chunk g of a contraction-contiguous row (swz layout), and
+// the two kinds of fragment can be paired in one MFMA.
+struct TrRead {
   template <class Lay>
   __device__ __forceinline__ static int off(int c, int lane) {
     const int g = lane >> 4, i = lane & 15;
-    const int m = 8 * g + (i >> 1);
-    return Lay::at(m, c) + 8 * (i & 1);
+    return Lay::at(16 * g + (i >> 1), c) + 8 * (i & 1);
   }
-  __device__ __forceinline__ void init(int lane, int wm, int wn) {
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) qoff[i] = off<QL>(wm * T::FM + i, lane);
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) poff[j] = off<PL>(wn * T::FN + j, lane);
-  }
+  // second: byte distance of 8 rows (8 * BT: sw and the block shift repeat)
   __device__ __forceinline__ static v4i frag(const int8_t *p, int second) {
     typedef int32_t v2i __attribute__((ext_vector_type(2)));
     typedef __attribute__((address_space(3))) v2i lds_v2i;
@@ -590,14 +610,58 @@ struct Frags<DW, T> {
     const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p + second));
     return v4i{lo.x, lo.y, hi.x, hi.y};
   }
+};
+
+// dX: Q (dC rows) contraction-contiguous in the swz layout, P (decoded W,
+// rows = contraction n) in a RowLayout, read transposed.
+template <class T>
+struct Frags<DX, T> {
+  typedef RowLayout<T::BN> PL;
+  int qoff, poff[T::FN];
+  __device__ __forceinline__ void init(int lane, int wm, int wn) {
+    qoff = wm * T::TM * LP + swz(lane & 15, lane >> 4);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) poff[j] = TrRead::off<PL>(wn * T::FN + j, lane);
+  }
   __device__ __forceinline__ void step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
                                        const int8_t *pb) const {
     v4i fp[T::FN];
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) fp[j] = frag(pb + poff[j], 32 * T::BN);
+    for (int j = 0; j < T::FN; ++j) fp[j] = TrRead::frag(pb + poff[j], 8 * T::BN);
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) mfma_block<T>(acc, fp, frag(qb + qoff[i], 32 * T::BM), i);
+    for (int i = 0; i < T::FM; ++i)
+      mfma_block<T>(acc, fp, *reinterpret_cast<const v4i *>(qb + qoff + i * 16 * LP), i);
   }
+};
+
+// dW: both operands in RowLayouts (rows = contraction m), both read transposed.
+template <class T>
+struct Frags<DW, T> {
+  typedef RowLayout<T::BM> QL;
+  typedef RowLayout<T::BN> PL;
+  int qoff[T::FM], poff[T::FN];
+  __device__ __forceinline__ void init(int lane, int wm, int wn) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) qoff[i] = TrRead::off<QL>(wm * T::FM + i, lane);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) poff[j] = TrRead::off<PL>(wn * T::FN + j, lane);
+  }
+  __device__ __forceinline__ void step(v4i (&acc)[T::FM][T::FN], const int8_t *qb,
+                                       const int8_t *pb) const {
+    v4i fp[T::FN];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) fp[j] = TrRead::frag(pb + poff[j], 8 * T::BN);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) mfma_block<T>(acc, fp, TrRead::frag(qb + qoff[i], 8 * T::BM), i);
+  }
+};
+
+// LDS bytes of one pipeline stage of each operand, and of the kernel's two stages.
+template <int OP, class T>
+struct StageBytes {
+  static constexpr int Q = OP == DW ? RowLayout<T::BM>::kBytes : T::BM * LP;
+  static constexpr int P = OP == FWD ? T::BN * LP : RowLayout<T::BN>::kBytes;
+  static constexpr int kLds = 2 * (Q + P);
 };
 
 // Store one 16x16 result block (this lane's 4 consecutive int32) at (row, col).
@@ -621,9 +685,10 @@ __device__ __forceinline__ void store_block(const Args &a, const v4i &v, int64_t
 template <int OP, class T, bool FAST>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(T::OCC)))
 void tgemm_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) int8_t smem[T::kLds];
-  int8_t *const sq = smem;                    // [2][BM][LP]
-  int8_t *const sp = smem + 2 * T::BM * LP;   // [2][BN][LP]
+  typedef StageBytes<OP, T> SB;
+  __shared__ __attribute__((aligned(16))) int8_t smem[SB::kLds];
+  int8_t *const sq = smem;               // two Q stages
+  int8_t *const sp = smem + 2 * SB::Q;   // two P stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -671,9 +736,8 @@ void tgemm_kernel(Args a) {
       st.load(slot[u], (int64_t)(j + T::PF) * BK, decltype(full)::value || j + T::PF < nfull);
       if constexpr (T::PIN) __builtin_amdgcn_sched_barrier(0);
       const int cur = j & 1;
-      fr.step(acc, sq + cur * T::BM * LP, sp + cur * T::BN * LP);
-      S::store(slot[(u + 1) % T::PF], sq + (cur ^ 1) * T::BM * LP, sp + (cur ^ 1) * T::BN * LP,
-               tid);
+      fr.step(acc, sq + cur * SB::Q, sp + cur * SB::P);
+      S::store(slot[(u + 1) % T::PF], sq + (cur ^ 1) * SB::Q, sp + (cur ^ 1) * SB::P, tid);
       lds_barrier();
     }
   };
@@ -720,7 +784,7 @@ void tgemm_kernel(Args a) {
 
 // Tile shapes per product.  Prefetch depth, occupancy and load pinning are
 // chosen per product from measured MI355X runs, such that no instantiation
-// spills registers (the dX stager holds 32 registers per slot).  At occupancy
+// spills registers.  At occupancy
 // 2 the dW accumulators stay in VGPRs; at 1 the compiler moves them to AGPRs
 // and copies them between sets every step.
 template <int OP>
@@ -733,7 +797,7 @@ struct Tiles<FWD> {
 };
 template <>
 struct Tiles<DX> {
-  typedef Tile<256, 128, 2, 2, 1, 2, true> L;
+  typedef Tile<256, 128, 2, 2, 2, 2, true> L;
   typedef Tile<128, 144, 4, 1, 1, 2, true> W;
   typedef Tile<64, 64, 2, 2, 2, 2, true> S;
 };
@@ -748,17 +812,28 @@ typedef Tiles<FWD> TileShapes;  // the shapes (not the tuning) are common
 enum TileId { TL = 0, TW = 1, TS = 2, kTiles = 3 };
 
 struct TileInfo {
-  int bm, bn, lds;
+  int bm, bn;
   double eff;  // relative MFMA efficiency (operand bytes per MAC read from LDS)
 };
 
 const TileInfo kTileInfo[kTiles] = {
     // efficiencies relative to the large tile, from measured MI355X runs
     // (operand bytes staged per MAC grow as the tile shrinks)
-    {TileShapes::L::BM, TileShapes::L::BN, TileShapes::L::kLds, 1.0},
-    {TileShapes::W::BM, TileShapes::W::BN, TileShapes::W::kLds, 0.8},
-    {TileShapes::S::BM, TileShapes::S::BN, TileShapes::S::kLds, 0.3},
+    {TileShapes::L::BM, TileShapes::L::BN, 1.0},
+    {TileShapes::W::BM, TileShapes::W::BN, 0.8},
+    {TileShapes::S::BM, TileShapes::S::BN, 0.3},
 };
+
+template <int OP>
+int lds_of_tile(int tile) {
+  return tile == TL   ? StageBytes<OP, typename Tiles<OP>::L>::kLds
+         : tile == TW ? StageBytes<OP, typename Tiles<OP>::W>::kLds
+                      : StageBytes<OP, typename Tiles<OP>::S>::kLds;
+}
+
+int lds_bytes(int op, int tile) {
+  return op == FWD ? lds_of_tile<FWD>(tile) : op == DX ? lds_of_tile<DX>(tile) : lds_of_tile<DW>(tile);
+}
 
 struct Shape {
   int64_t R, Cc, L;
@@ -844,7 +919,7 @@ int check_dims(int op, int64_t M, int64_t N, int64_t K) {
 bool fast_ok(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t palign) {
   (void)M;
   if (op == FWD) return K % 16 == 0 && qalign % 16 == 0 && palign % 4 == 0;
-  if (op == DX) return N % 16 == 0 && qalign % 16 == 0;
+  if (op == DX) return N % 16 == 0 && K % 16 == 0 && qalign % 16 == 0 && palign % 4 == 0;
   return K % 16 == 0 && N % 16 == 0 && qalign % 16 == 0 && palign % 16 == 0;
 }
 
@@ -952,7 +1027,8 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
-  const TileInfo &ti = kTileInfo[pick_tile(s)];
+  const int tile = pick_tile(s);
+  const TileInfo &ti = kTileInfo[tile];
   memset(plan, 0, sizeof(*plan));
   plan->out_rows = s.R;
   plan->out_cols = s.Cc;
@@ -963,7 +1039,7 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->workgroups = plan->tiles;
   plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
   plan->threads_per_workgroup = kThreads;
-  plan->lds_bytes = ti.lds;
+  plan->lds_bytes = lds_bytes(op, tile);
   const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   return TGEMM_OK;

@@ -9,12 +9,12 @@ FWD_SHAPES = [
     (300, 272, 96), (299, 271, 100),       # 64 x 64
     (1, 1, 4), (1, 4097, 36), (1000, 1, 64), (65, 65, 68)]
 
-DX_SHAPES = [  # contraction N
-    (8200, 80, 3900), (8200, 84, 3900),
-    (4100, 80, 900), (4100, 84, 900),
-    (4100, 80, 3900), (4100, 84, 3900),
+DX_SHAPES = [  # contraction N; the fast path needs N % 16 == K % 16 == 0
+    (8200, 80, 3904), (8200, 84, 3900),
+    (4100, 80, 912), (4100, 84, 900),
+    (4100, 80, 3904), (4100, 84, 3900),
     (300, 96, 272), (299, 100, 268),
-    (1, 1, 4), (27, 3456, 1280), (1, 4, 4100)]
+    (1, 1, 4), (1, 16, 16), (27, 3456, 1280), (1, 4, 4100)]
 
 DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
     (80, 3904, 8208), (81, 3901, 8201),
