@@ -31,9 +31,9 @@
  *   - On success the work is enqueued on `stream` (NULL: the default stream)
  *     and the call returns without waiting.  Faults that only show while the
  *     kernel runs surface at the caller's next synchronisation.
- *   - Results are exact: integer sums in int32, each output reduced serially
- *     over the whole contraction inside one workgroup (no split of the
- *     contraction, no atomics), so repeated calls give identical bits.
+ *   - Results are exact: integer sums in int32, each output reduced over the
+ *     whole contraction inside one workgroup in a fixed order (no split
+ *     across workgroups, no atomics), so repeated calls give identical bits.
  *   - Calls are thread-safe; concurrent calls on different streams may run at
  *     the same time as long as their outputs do not overlap.
  */
@@ -112,12 +112,17 @@ const char *ternary_gemm_status_str(int status);
  * touching the device (for tests and tooling).  op: 0 forward, 1 dX, 2 dW.
  * Fills the output tile (rows x cols of the row-major output per workgroup),
  * the number of tiles and of workgroups (one tile each), the tile columns per
- * band of the workgroup -> tile order (see ternary_gemm_tile_of_block), the LDS bytes per
- * workgroup and whether the fast (vector-load) path applies given the base
- * alignments passed in `align` (the smallest power-of-two alignment of the
- * input pointers, in bytes).  Returns TGEMM_OK, or the status the real call
- * would return for these dimensions (pointer checks excepted).
+ * band of the workgroup -> tile order (see ternary_gemm_tile_of_block),
+ * whether the fast (vector-load) path applies given the base alignments
+ * passed in `align` (the smallest power-of-two alignment of the input
+ * pointers, in bytes), which kernel runs (TGEMM_KERNEL_*), and that kernel's
+ * threads and LDS bytes per workgroup.  Returns TGEMM_OK, or the status the
+ * real call would return for these dimensions (pointer checks excepted).
  */
+#define TGEMM_KERNEL_TILED 0   /* one 4-wave workgroup per output tile          */
+#define TGEMM_KERNEL_SPLIT 2   /* dW: the tile's contraction split between two
+                                  4-wave halves of one workgroup              */
+
 typedef struct tgemm_plan {
     int64_t out_rows, out_cols, contraction;
     int32_t tile_rows, tile_cols;
@@ -127,6 +132,7 @@ typedef struct tgemm_plan {
     int32_t threads_per_workgroup;
     int32_t lds_bytes;
     int32_t fast_path;
+    int32_t kernel;
 } tgemm_plan;
 
 int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align,

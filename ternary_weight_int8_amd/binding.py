@@ -35,8 +35,11 @@ class TgemmPlan(ctypes.Structure):
         ("workgroups", ctypes.c_int64),
         ("band_cols", ctypes.c_int32),
         ("threads_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-        ("fast_path", ctypes.c_int32),
+        ("fast_path", ctypes.c_int32), ("kernel", ctypes.c_int32),
     ]
+
+
+KERNEL_TILED, KERNEL_SPLIT = 0, 2   # TgemmPlan.kernel
 
 
 class TernaryGemmError(RuntimeError):

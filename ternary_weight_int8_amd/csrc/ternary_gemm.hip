@@ -45,8 +45,10 @@
 // Exactness: every partial sum is bounded by the final bound the host checks
 // (L * 128 for ternary, L * 128^2 for int8 x int8), so int32 accumulation in
 // any order is exact [P10425 "What this adds", "i32 overflow bound"; P10855
-// PR body, "k <= 131071"].  The contraction is reduced serially inside one
-// workgroup: no split of it, no atomics, identical bits on every call.
+// PR body, "k <= 131071"].  Each output is reduced inside one workgroup, in a
+// fixed order (dW at long contractions in two interleaved halves that are
+// added at the end): no split across workgroups, no atomics, identical bits
+// on every call.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -86,6 +88,7 @@ template <bool B>
 struct Flag {
   static constexpr bool value = B;
 };
+
 
 struct Args {
   const int8_t *q;    // Q source
@@ -337,9 +340,6 @@ struct RowCopyOp {
   __device__ __forceinline__ static bool has(int i, int wave) {
     return kUnits % kThreads == 0 || i * kThreads + wave * 64 < kUnits;
   }
-  __device__ __forceinline__ static int wave_id() {
-    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  }
 
   __device__ __forceinline__ void init(const int8_t *src, int64_t ld_, int64_t nout_, int64_t L_,
                                        int64_t t0, int tid) {
@@ -385,7 +385,7 @@ struct RowCopyOp {
   }
 
   __device__ __forceinline__ static void store(const Slot &s, int8_t *lds, int tid) {
-    const int wave = wave_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       if (!has(i, wave)) break;
@@ -664,21 +664,39 @@ struct StageBytes {
   static constexpr int kLds = 2 * (Q + P);
 };
 
-// Store one 16x16 result block (this lane's 4 consecutive int32) at (row, col).
-__device__ __forceinline__ void store_block(const Args &a, const v4i &v, int64_t row, int64_t col,
-                                            bool interior) {
-  if (interior) {
-    *reinterpret_cast<v4i *>(a.out + row * a.Cc + col) = v;
+// Epilogue: lane holds O[row][col .. col+3] of each 16x16 block of a wave's
+// sub-tile starting at (r0, c0); `inside` says the workgroup's whole tile is
+// inside the output.
+template <class T>
+__device__ __forceinline__ void store_tile(const Args &a, const v4i (&acc)[T::FM][T::FN], int64_t r0,
+                                           int64_t c0, bool inside, int lane) {
+  const int64_t rbase = r0 + (lane & 15);
+  const int64_t cbase = c0 + (lane >> 4) * 4;
+  if (a.vec_out && inside) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      int32_t *orow = a.out + (rbase + i * 16) * a.Cc + cbase;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) *reinterpret_cast<v4i *>(orow + j * 16) = acc[i][j];
+    }
     return;
   }
-  if (row >= a.R) return;
-  int32_t *o = a.out + row * a.Cc;
-  if (a.vec_out && col + 3 < a.Cc) {
-    *reinterpret_cast<v4i *>(o + col) = v;
-  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (col + e < a.Cc) o[col + e] = v[e];
+  for (int i = 0; i < T::FM; ++i) {
+    const int64_t row = rbase + i * 16;
+    if (row >= a.R) continue;
+    int32_t *orow = a.out + row * a.Cc;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int64_t col = cbase + j * 16;
+      if (a.vec_out && col + 3 < a.Cc) {
+        *reinterpret_cast<v4i *>(orow + col) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < a.Cc) orow[col + e] = acc[i][j][e];
+      }
+    }
   }
 }
 
@@ -747,35 +765,8 @@ void tgemm_kernel(Args a) {
   for (; g < gfull; ++g) group(g, Flag<true>());
   for (; g < ngroups; ++g) group(g, Flag<false>());
 
-  // epilogue: lane holds O[row][col .. col+3] of each 16x16 block
-  const int64_t rbase = q0 + wm * T::TM + (lane & 15);
-  const int64_t cbase = p0 + wn * T::TN + (lane >> 4) * 4;
-  if (a.vec_out && q0 + T::BM <= a.R && p0 + T::BN <= a.Cc) {  // interior tile
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      int32_t *orow = a.out + (rbase + i * 16) * a.Cc + cbase;
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) *reinterpret_cast<v4i *>(orow + j * 16) = acc[i][j];
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) {
-    const int64_t row = rbase + i * 16;
-    if (row >= a.R) continue;
-    int32_t *orow = a.out + row * a.Cc;
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int64_t col = cbase + j * 16;
-      if (a.vec_out && col + 3 < a.Cc) {
-        *reinterpret_cast<v4i *>(orow + col) = acc[i][j];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < a.Cc) orow[col + e] = acc[i][j][e];
-      }
-    }
-  }
+  store_tile<T>(a, acc, q0 + wm * T::TM, p0 + wn * T::TN, q0 + T::BM <= a.R && p0 + T::BN <= a.Cc,
+                lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,9 +822,6 @@ int lds_of_tile(int tile) {
                       : StageBytes<OP, typename Tiles<OP>::S>::kLds;
 }
 
-int lds_bytes(int op, int tile) {
-  return op == FWD ? lds_of_tile<FWD>(tile) : op == DX ? lds_of_tile<DX>(tile) : lds_of_tile<DW>(tile);
-}
 
 struct Shape {
   int64_t R, Cc, L;
@@ -928,6 +916,101 @@ uintptr_t align_of(const void *p) {
   return v ? (v & (~v + 1)) : ((uintptr_t)1 << 20);
 }
 
+// ---------------------------------------------------------------------------
+// dW with the contraction split inside the workgroup.  dW's output is small
+// (K x N) and its contraction long (M), so at the large shapes there are only
+// about as many tiles as CUs: one 4-wave workgroup per CU leaves each SIMD a
+// single wave, whose MFMAs stop at every barrier and LDS wait.  Here a
+// workgroup has two 4-wave halves on the same tile: half h takes the
+// contraction steps j = 2t + h, each half with its own LDS stages, so every
+// SIMD runs two waves.  At the end half 1 hands its int32 sums to half 0
+// through LDS and half 0 adds and stores them: a fixed order, so the result
+// is exact and identical on every call, with no atomics and no scratch memory.
+// ---------------------------------------------------------------------------
+template <class T, bool FAST>
+__global__ __attribute__((amdgpu_flat_work_group_size(2 * kThreads, 2 * kThreads), amdgpu_waves_per_eu(2)))
+void tgemm_dw_split(Args a) {
+  typedef StageBytes<DW, T> SB;
+  constexpr int kHalf = 2 * (SB::Q + SB::P);                      // a half's two stages
+  constexpr int kRed = T::FM * T::FN * kThreads * 16;             // half 1's sums
+  constexpr int kBytes = 2 * kHalf > kRed ? 2 * kHalf : kRed;
+  __shared__ __attribute__((aligned(16))) int8_t smem[kBytes];
+
+  const int h = (int)(threadIdx.x >> 8);         // half (wave-uniform)
+  const int tid = (int)(threadIdx.x & (kThreads - 1));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  int8_t *const sq = smem + h * kHalf;
+  int8_t *const sp = sq + 2 * SB::Q;
+
+  int32_t tr, tc;
+  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles), a.tiles / a.tiles_c, a.tiles_c, a.band_cols, &tr,
+          &tc);
+  const int64_t q0 = (int64_t)tr * T::BM;
+  const int64_t p0 = (int64_t)tc * T::BN;
+
+  v4i acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  typedef Stages<DW, T, FAST> S;
+  S st;
+  st.init(a, q0, p0, tid);
+  typename S::Slot slot[T::PF];
+  Frags<DW, T> fr;
+  fr.init(lane, wm, wn);
+
+  const int32_t nk = (int32_t)((a.L + BK - 1) / BK);
+  const int32_t nfull = (int32_t)(a.L / BK);
+  const int32_t nt = (nk + 1) / 2;                        // steps per half (same for both)
+  const int32_t ngroups = (nt + T::PF - 1) / T::PF;
+  auto c0_of = [&](int32_t t) { return (int64_t)(2 * t + h) * BK; };
+  auto full_of = [&](int32_t t) { return 2 * t + h < nfull; };
+
+#pragma unroll
+  for (int s = 0; s < T::PF; ++s) st.load(slot[s], c0_of(s), full_of(s));
+  S::store(slot[0], sq, sp, tid);
+  lds_barrier();
+
+  auto group = [&](int32_t g, auto full) {
+#pragma unroll
+    for (int u = 0; u < T::PF; ++u) {
+      const int32_t t = g * T::PF + u;
+      st.load(slot[u], c0_of(t + T::PF), decltype(full)::value || full_of(t + T::PF));
+      if constexpr (T::PIN) __builtin_amdgcn_sched_barrier(0);
+      const int cur = t & 1;
+      fr.step(acc, sq + cur * SB::Q, sp + cur * SB::P);
+      S::store(slot[(u + 1) % T::PF], sq + (cur ^ 1) * SB::Q, sp + (cur ^ 1) * SB::P, tid);
+      lds_barrier();
+    }
+  };
+  // groups whose loads (half steps up to (g + 2) * PF - 1, i.e. steps up to
+  // 2 ((g + 2) PF - 1) + 1) are all full, for both halves
+  const int32_t gfull = nfull / (2 * T::PF) - 1 > 0 ? nfull / (2 * T::PF) - 1 : 0;
+  int32_t g = 0;
+  for (; g < gfull; ++g) group(g, Flag<true>());
+  for (; g < ngroups; ++g) group(g, Flag<false>());
+
+  // half 1 -> LDS -> half 0 (the last barrier above ends every read of the stages)
+  v4i *red = reinterpret_cast<v4i *>(smem);
+  if (h == 1) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) red[(i * T::FN + j) * kThreads + tid] = acc[i][j];
+  }
+  lds_barrier();
+  if (h == 1) return;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] += red[(i * T::FN + j) * kThreads + tid];
+  store_tile<T>(a, acc, q0 + wm * T::TM, p0 + wn * T::TN, q0 + T::BM <= a.R && p0 + T::BN <= a.Cc,
+                lane);
+}
+
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -939,8 +1022,48 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
   return fast ? launch_t<OP, T, true>(a, stream) : launch_t<OP, T, false>(a, stream);
 }
 
+
+// Kernel per product, tile and load path:
+//   tiled  tgemm_kernel: every case but the next
+//   split  tgemm_dw_split: dW, 128 x 144 tile, contraction of 8 steps or more
+// (A variant that loads the int8 operand of the forward and dX straight into
+// MFMA registers, without LDS, measured no faster in the three-product step
+// on MI355X and was left out.)
+enum KernelId { KTILED = 0, KSPLIT = 2 };
+
+int pick_kernel(int op, int tile, int64_t L) {
+  if (op == DW && tile == TW && L >= 8 * BK) return KSPLIT;
+  return KTILED;
+}
+
 template <int OP>
-hipError_t launch_op(const Args &a, int tile, bool fast, hipStream_t stream) {
+int lds_of_kernel(int kernel, int tile) {
+  if (kernel == KSPLIT) {
+    typedef StageBytes<DW, Tiles<DW>::W> SB;
+    const int stages = 4 * (SB::Q + SB::P), red = Tiles<DW>::W::FM * Tiles<DW>::W::FN * kThreads * 16;
+    return stages > red ? stages : red;
+  }
+  return lds_of_tile<OP>(tile);
+}
+
+int kernel_lds(int op, int kernel, int tile) {
+  return op == FWD ? lds_of_kernel<FWD>(kernel, tile)
+         : op == DX ? lds_of_kernel<DX>(kernel, tile)
+                    : lds_of_kernel<DW>(kernel, tile);
+}
+
+template <int OP>
+hipError_t launch_op(const Args &a, int kernel, int tile, bool fast, hipStream_t stream) {
+  if constexpr (OP == DW) {
+    if (kernel == KSPLIT) {
+      typedef typename Tiles<DW>::W T;
+      if (fast)
+        hipLaunchKernelGGL((tgemm_dw_split<T, true>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((tgemm_dw_split<T, false>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   switch (tile) {
     case TL: return launch_f<OP, typename Tiles<OP>::L>(a, fast, stream);
     case TW: return launch_f<OP, typename Tiles<OP>::W>(a, fast, stream);
@@ -977,13 +1100,14 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
+  const int kernel = pick_kernel(op, tile, s.L);
   hipError_t e;
   if (op == FWD)
-    e = launch_op<FWD>(a, tile, fast, stream);
+    e = launch_op<FWD>(a, kernel, tile, fast, stream);
   else if (op == DX)
-    e = launch_op<DX>(a, tile, fast, stream);
+    e = launch_op<DX>(a, kernel, tile, fast, stream);
   else
-    e = launch_op<DW>(a, tile, fast, stream);
+    e = launch_op<DW>(a, kernel, tile, fast, stream);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
 
@@ -1038,10 +1162,11 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
   plan->workgroups = plan->tiles;
   plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
-  plan->threads_per_workgroup = kThreads;
-  plan->lds_bytes = lds_bytes(op, tile);
   const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
+  plan->kernel = pick_kernel(op, tile, s.L);
+  plan->threads_per_workgroup = plan->kernel == KSPLIT ? 2 * kThreads : kThreads;
+  plan->lds_bytes = kernel_lds(op, plan->kernel, tile);
   return TGEMM_OK;
 }
 

@@ -21,6 +21,7 @@ DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
     (80, 912, 4112), (80, 901, 4101),
     (80, 3904, 4112), (80, 3901, 4101),
     (96, 272, 304), (97, 271, 299),
-    (1, 1, 1), (1782, 5, 7), (1782, 16, 16), (27, 3456, 1280)]
+    (1, 1, 1), (1782, 5, 7), (1782, 16, 16), (27, 3456, 1280),
+    (1088, 912, 4112), (1000, 901, 4101)]   # long contractions: the split dW kernel
 
 TILES = ((256, 128), (128, 144), (64, 64))

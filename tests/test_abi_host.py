@@ -114,21 +114,36 @@ def _coverage(op, M, N, K):
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
-    assert pl.threads_per_workgroup == 256
+    assert pl.threads_per_workgroup == (512 if pl.kernel == B.KERNEL_SPLIT else 256)
     assert pl.lds_bytes <= 160 * 1024
     assert pl.workgroups == pl.tiles
 
 
 def test_parity_shapes_reach_every_tile_and_path():
-    # the GPU parity shape lists exercise every tile shape on both load paths
+    # the GPU parity shape lists exercise every tile shape on both load paths,
+    # and every kernel on each load path it serves
+    kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1)},
+               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1)},
+               "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
+                      (B.KERNEL_SPLIT, 1)}}
     for op, shapes in (("fwd", FWD_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
-        seen = set()
+        seen, seen_k = set(), set()
         for s in shapes:
             pl = B.plan(op, *s)
             seen.add((pl.tile_rows, pl.tile_cols, pl.fast_path))
+            seen_k.add((pl.kernel, pl.fast_path))
         for tile in TILES:
             for fast in (0, 1):
                 assert (*tile, fast) in seen, (op, tile, fast)
+        assert kernels[op] <= seen_k, (op, kernels[op] - seen_k)
+
+
+def test_kernel_choice():
+    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_TILED
+    assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_TILED
+    assert B.plan("dw", 16384, 3456, 1280).kernel == B.KERNEL_SPLIT
+    assert B.plan("dw", 80, 3904, 4112).kernel == B.KERNEL_TILED   # short contraction
+    assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
 
 
 def test_block_out_of_range():
