@@ -110,24 +110,32 @@ const char *ternary_gemm_status_str(int status);
 /*
  * Launch plan the library would use for a call, computed on the host without
  * touching the device (for tests and tooling).  op: 0 forward, 1 dX, 2 dW.
- * Fills the output tile (rows x cols of the row-major output per workgroup),
- * the number of tiles and of workgroups (one tile each), the tile columns per
- * band of the workgroup -> tile order (see ternary_gemm_tile_of_block),
- * whether the fast (vector-load) path applies given the base alignments
- * passed in `align` (the smallest power-of-two alignment of the input
- * pointers, in bytes), which kernel runs (TGEMM_KERNEL_*), and that kernel's
- * threads and LDS bytes per workgroup.  Returns TGEMM_OK, or the status the
- * real call would return for these dimensions (pointer checks excepted).
+ * Fills the output tile (rows x cols of the row-major output computed at a
+ * time by one workgroup), the number of tiles, the number of workgroups
+ * launched and the most tiles any one of them computes (1 for the one-tile
+ * kernels; persistent kernels loop over several), the tile columns per band
+ * of the one-tile kernels' workgroup -> tile order, whether the fast
+ * (vector-load) path applies given the base alignments passed in `align`
+ * (the smallest power-of-two alignment of the input pointers, in bytes),
+ * which kernel runs (TGEMM_KERNEL_*), and that kernel's threads and LDS bytes
+ * per workgroup.  Returns TGEMM_OK, or the status the real call would return
+ * for these dimensions (pointer checks excepted).
  */
 #define TGEMM_KERNEL_TILED 0   /* one 4-wave workgroup per output tile          */
 #define TGEMM_KERNEL_SPLIT 2   /* dW: the tile's contraction split between two
                                   4-wave halves of one workgroup              */
+#define TGEMM_KERNEL_STREAM 3  /* forward, K % 64 == 0, 16-byte aligned A and
+                                  4-byte aligned Wpacked, M*K and N*K/4 below
+                                  2^31, at least 256 tiles of 256 x 288: one
+                                  persistent 8-wave workgroup per CU, operands
+                                  loaded straight into LDS                    */
 
 typedef struct tgemm_plan {
     int64_t out_rows, out_cols, contraction;
     int32_t tile_rows, tile_cols;
     int64_t tiles;
     int64_t workgroups;
+    int64_t tiles_per_workgroup;
     int32_t band_cols;
     int32_t threads_per_workgroup;
     int32_t lds_bytes;
@@ -139,14 +147,18 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align,
                       tgemm_plan *plan);
 
 /*
- * Output tile handled by workgroup `block` under a plan (host mirror of the
- * kernel's own workgroup -> tile order: each of the chip's eight L2 slices
- * gets a contiguous run of a tile order that goes row by row inside bands of
- * band_cols tile columns, so tiles sharing input rows and columns share an L2).  Writes the tile's first output
- * row and column.  Returns TGEMM_OK, or TGEMM_ERR_DIM if block is out of range.
+ * Output tile that workgroup `workgroup` computes in its iteration
+ * `iteration` (0 .. tiles_per_workgroup - 1) under a plan: a host mirror of
+ * the kernels' own workgroup -> tile order.  That order gives each of the
+ * chip's eight L2 slices (XCDs; workgroup b runs on XCD b % 8) a contiguous
+ * run of tiles, row by row (inside bands of band_cols tile columns for the
+ * one-tile kernels), so tiles in flight together on one XCD share input rows
+ * and columns in its L2.  Writes the tile's first output row and column.
+ * Returns TGEMM_OK, or TGEMM_ERR_DIM if the workgroup is out of range or
+ * computes no tile in that iteration.
  */
-int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block,
-                               int64_t *row0, int64_t *col0);
+int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iteration,
+                         int64_t *row0, int64_t *col0);
 
 #ifdef __cplusplus
 }

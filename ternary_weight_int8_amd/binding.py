@@ -21,7 +21,7 @@ EXPORTS = (
     "ternary_gemm_s8_dw",
     "ternary_gemm_status_str",
     "ternary_gemm_plan",
-    "ternary_gemm_tile_of_block",
+    "ternary_gemm_tile_of",
 )
 
 OPS = {"fwd": 0, "dx": 1, "dw": 2}
@@ -33,13 +33,14 @@ class TgemmPlan(ctypes.Structure):
         ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
         ("tiles", ctypes.c_int64),
         ("workgroups", ctypes.c_int64),
+        ("tiles_per_workgroup", ctypes.c_int64),
         ("band_cols", ctypes.c_int32),
         ("threads_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
         ("fast_path", ctypes.c_int32), ("kernel", ctypes.c_int32),
     ]
 
 
-KERNEL_TILED, KERNEL_SPLIT = 0, 2   # TgemmPlan.kernel
+KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM = 0, 2, 3   # TgemmPlan.kernel
 
 
 class TernaryGemmError(RuntimeError):
@@ -68,9 +69,9 @@ def lib():
         L.ternary_gemm_status_str.restype = ctypes.c_char_p
         L.ternary_gemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.POINTER(TgemmPlan)]
         L.ternary_gemm_plan.restype = ctypes.c_int
-        L.ternary_gemm_tile_of_block.argtypes = [ctypes.POINTER(TgemmPlan), i64,
-                                                 ctypes.POINTER(i64), ctypes.POINTER(i64)]
-        L.ternary_gemm_tile_of_block.restype = ctypes.c_int
+        L.ternary_gemm_tile_of.argtypes = [ctypes.POINTER(TgemmPlan), i64, i64,
+                                           ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.ternary_gemm_tile_of.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -92,11 +93,15 @@ def plan(op: str, M: int, N: int, K: int, align: int = 256):
     return pl
 
 
-def tile_of_block(pl: TgemmPlan, block: int):
+def tile_of(pl: TgemmPlan, workgroup: int, iteration: int = 0):
+    """(row0, col0) of the tile a workgroup computes in one iteration, or None if none."""
     r, c = ctypes.c_int64(), ctypes.c_int64()
-    st = lib().ternary_gemm_tile_of_block(ctypes.byref(pl), block, ctypes.byref(r), ctypes.byref(c))
+    st = lib().ternary_gemm_tile_of(ctypes.byref(pl), workgroup, iteration, ctypes.byref(r),
+                                    ctypes.byref(c))
+    if st == ERR_DIM and 0 <= workgroup < pl.workgroups and 0 <= iteration < pl.tiles_per_workgroup:
+        return None
     if st != OK:
-        raise TernaryGemmError("ternary_gemm_tile_of_block", st, status_str(st))
+        raise TernaryGemmError("ternary_gemm_tile_of", st, status_str(st))
     return r.value, c.value
 
 

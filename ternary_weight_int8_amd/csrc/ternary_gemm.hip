@@ -129,28 +129,26 @@ __host__ __device__ inline void tile_rc(int32_t pos, int32_t tiles_r, int32_t ti
 }
 
 // ---------------------------------------------------------------------------
-// Code decode.  spread4 moves the four 2-bit codes of a byte into the low
-// bits of four bytes; v_perm_b32 then uses each byte as a selector into
-// kCodeTable, turning four codes into four int8 weights in one instruction.
+// Code decode: one packed dword x (code i at bits 2i) -> 16 int8 weights.
+// For output dword j (codes 4j .. 4j + 3, byte j of x), one v_perm_b32
+// gathers byte j of x and byte j of y = x >> 2 as [x_j, y_j, x_j, y_j]; a
+// packed 16-bit right shift by (0, 4) leaves code 4j + k in the low two bits
+// of byte k (byte 1: bits 2-3 of x_j, byte 2: bits 4-5, byte 3: bits 6-7);
+// masked to those bits, each byte selects its weight from kCodeTable with a
+// second v_perm_b32.  Four codes -> four weights in four instructions.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t spread4(uint32_t b) {
-  uint32_t t = b | (b << 6);        // codes 0,1 -> bits 0-1, 8-9
-  t = t | (t << 12);                // codes 2,3 -> bits 16-17, 24-25
-  return t & 0x03030303u;
-}
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t weights4(uint32_t sel) {
-  // v_perm_b32(src0=0, src1=table): selector values 0..3 pick bytes of src1
-  return __builtin_amdgcn_perm(0u, kCodeTable, sel);
-}
-
-// 16 codes of one packed dword (code i at bits 2i) -> 16 int8 weights, in order
 __device__ __forceinline__ v4i decode16(uint32_t x) {
+  const uint32_t y = x >> 2;
   v4i w;
-  w[0] = (int32_t)weights4(spread4(x & 0xFFu));
-  w[1] = (int32_t)weights4(spread4((x >> 8) & 0xFFu));
-  w[2] = (int32_t)weights4(spread4((x >> 16) & 0xFFu));
-  w[3] = (int32_t)weights4(spread4(x >> 24));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // selector bytes [j, 4 + j, j, 4 + j]: bytes 0-3 of the pool are x, 4-7 are y
+    const uint32_t sel = (uint32_t)j * 0x00010001u + (uint32_t)(4 + j) * 0x01000100u;
+    const u16x2 h = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(y, x, sel)) >> (u16x2){0, 4};
+    w[j] = (int32_t)__builtin_amdgcn_perm(0u, kCodeTable, __builtin_bit_cast(uint32_t, h) & 0x03030303u);
+  }
   return w;
 }
 
@@ -1011,6 +1009,340 @@ void tgemm_dw_split(Args a) {
                 lane);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming forward kernel (large outputs, K % 64 == 0, aligned operands).
+//
+// One workgroup of 8 waves per CU, persistent over its tiles of 256 x 288
+// outputs (16384 x 3456 splits into 768 such tiles: three per CU).  The waves
+// form a 4 x 2 grid of 64 x 144 sub-tiles, two waves per SIMD.
+//
+// Staging goes straight from global memory into LDS (never through VGPRs):
+// A rows with 16-byte loads and packed weight rows with 4-byte loads, issued
+// S - 1 steps ahead into a ring of S stages.  Each wave decodes the packed
+// dwords it loaded itself (16 codes -> one 16-byte chunk, the table lookup
+// of decode16) into a ring of three decoded stages, two steps ahead, so the
+// codes are decoded once per tile load [P10425 "What this adds"] and the
+// decode needs only the wave's own load count, no extra barrier.
+//
+// Register pipeline: during the MFMAs of step g a wave reads the A fragments
+// and the first weight fragment of step g + 1 (A fragments stay in registers
+// for the whole step; weight fragments stream through, one ahead), so the
+// MFMA issue never waits for LDS at a step boundary.  Hence the barrier that
+// starts step g publishes A(g + 1) and decoded W(g + 1).
+//
+// The loads come from inline assembly, so the compiler does not drain them
+// at every LDS read; each wave waits for its own loads with explicit vmcnt
+// counts (memory operations of a wave complete in issue order, so vmcnt(N),
+// N = the operations issued after the awaited one, is exactly that wait):
+//
+//   step g  top:  issue batch B(g + 3) = packed W then A of step g + 3
+//           mid:  wait for the packed W of step g + 2, decode it
+//           end:  wait for A(g + 2); barrier
+//
+// A tile's output is stored right after its last step, while loads of the
+// next tile are in flight; its kStores stores are younger than what the next
+// three waits await, and those waits count them.  The last steps re-load
+// the final step (valid addresses, never used), which keeps the counts
+// uniform; the kernel waits for every load before it ends, so no transfer
+// into LDS outlives it.
+// ---------------------------------------------------------------------------
+namespace fs {
+
+constexpr int BM = 256, BN = 288, S = 4;          // tile, LDS stages of loads
+constexpr int DS = 3;                             // decoded weight stages
+constexpr int kWaves = 8, kNT = 64 * kWaves;
+constexpr int WN = 2, TM = 64, TN = 144;          // wave grid 4 x 2
+constexpr int FM = TM / 16, FN = TN / 16;
+constexpr int kAStage = BM * LP;                  // A rows of one step
+constexpr int kWdStage = BN * LP;                 // decoded weights of one step
+constexpr int kALoads = kAStage / 1024 / kWaves;  // 16-byte loads per wave per step
+constexpr int kWpLoads = 3;                       // 4-byte loads per wave per step
+constexpr int kWpStage = kWaves * kWpLoads * 256; // packed rows (BN * 16 used)
+constexpr int kWpUnits = BN * 16 / 256;           // 4-byte loads that carry codes
+// Units (and so their decode) per wave: q or q + 1, the extra ones on the
+// last waves; waves w and w + 4 share a SIMD, so per-SIMD decode work differs
+// by at most one unit.
+constexpr int kUnitQ = kWpUnits / kWaves, kUnitR = kWpUnits % kWaves;
+__host__ __device__ constexpr int units_of(int w) { return kUnitQ + (w >= kWaves - kUnitR ? 1 : 0); }
+__host__ __device__ constexpr int first_unit(int w) {
+  return kUnitQ * w + (w > kWaves - kUnitR ? w - (kWaves - kUnitR) : 0);
+}
+constexpr int kOffWd = S * kAStage;
+constexpr int kOffWp = kOffWd + DS * kWdStage;
+constexpr int kLds = kOffWp + S * kWpStage;
+constexpr int kBatch = kALoads + kWpLoads;
+constexpr int kStores = FM * FN;
+constexpr int kWaitMid = kALoads + kBatch;        // A(g + 2), B(g + 3)
+constexpr int kWaitEnd = kBatch;                  // B(g + 3)
+static_assert(BM == TM * (kWaves / WN) && BN == TN * WN, "wave grid");
+static_assert(kALoads * kWaves * 1024 == kAStage, "A stage = whole 1 KB wave loads");
+static_assert(BN * 16 % 256 == 0 && kUnitQ + (kUnitR ? 1 : 0) <= kWpLoads, "packed stage");
+static_assert(first_unit(kWaves - 1) + units_of(kWaves - 1) == kWpUnits, "units");
+static_assert(kLds <= 160 * 1024, "LDS");
+static_assert(S == 4 && kWaitMid + kStores <= 63, "vmcnt field");
+static_assert(FN > FM, "A fragments of the next step are read during the first FM columns");
+
+// 16 bytes per lane from sbase + voff into LDS at lds + 16 * lane
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// 4 bytes per lane from sbase + voff into LDS at lds + 4 * lane
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// wait until at most N of this wave's memory operations are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// the same, then this wave's LDS operations, then meet the other waves
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+}  // namespace fs
+
+struct SArgs {
+  const int8_t *A;
+  const uint8_t *Wp;
+  int32_t *C;
+  int32_t M, N, K, kb;          // kb = K / 4, the packed row stride
+  int32_t tiles_r, tiles_c, band_cols, tiles;
+  int32_t nk;                   // steps per tile (K / 64)
+  int32_t vec_out;
+};
+
+// The decode of a wave's own packed dwords, in two halves so that the reads
+// can go out well before their results are used: fs_decode_read fetches the
+// dwords (16 codes each), fs_decode_write turns each into a 16-byte chunk of
+// int8 weights (decode16) and stores it in the decoded stage.
+__device__ __forceinline__ void fs_decode_read(uint32_t (&x)[fs::kWpLoads], const int8_t *src, int wave,
+                                               int lane) {
+  using namespace fs;
+#pragma unroll
+  for (int i = 0; i < kWpLoads; ++i)
+    if (i < units_of(wave))
+      x[i] = *reinterpret_cast<const uint32_t *>(src + 256 * (kWpLoads * wave + i) + 4 * lane);
+}
+__device__ __forceinline__ void fs_decode_write(const uint32_t (&x)[fs::kWpLoads], int8_t *dst, int wave,
+                                                int lane) {
+  using namespace fs;
+#pragma unroll
+  for (int i = 0; i < kWpLoads; ++i)
+    if (i < units_of(wave)) {
+      const int d = 64 * (first_unit(wave) + i) + lane;  // packed dword of the step: row d / 4
+      *reinterpret_cast<v4i *>(dst + swz(d >> 2, d & 3)) = decode16(x[i]);
+    }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(fs::kNT, fs::kNT), amdgpu_waves_per_eu(2)))
+void tgemm_fwd_stream(SArgs a) {
+  using namespace fs;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kLds];
+  const uint32_t lbase = (uint32_t)(uintptr_t)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Tiles of this workgroup: the tile positions (row-major over the tile
+  // grid) are split into eight contiguous runs, one per XCD (workgroup b runs
+  // on XCD b % 8), and the nx workgroups of an XCD take every nx-th position
+  // of its run, so the tiles an XCD works on at one time share A rows and
+  // the weight columns in its L2.
+  const int32_t nx = (int32_t)gridDim.x / 8, xcd = (int32_t)blockIdx.x % 8, j0 = (int32_t)blockIdx.x / 8;
+  const int32_t q8 = a.tiles / 8, r8 = a.tiles % 8;
+  const int32_t start = xcd * q8 + (xcd < r8 ? xcd : r8) + j0;
+  const int32_t cnt = q8 + (xcd < r8 ? 1 : 0);
+  const int32_t ntile = cnt > j0 ? (cnt - j0 + nx - 1) / nx : 0;
+  if (ntile == 0) return;
+
+  // Load offsets of a tile.  A load i of this wave fills tile rows
+  // 16 L .. 16 L + 15 (L = kALoads * wave + i); lane l lands in slot l % 4 of
+  // row 16 L + l / 4 and so fetches the chunk the swizzle puts there.  Packed
+  // load i fills slot kWpLoads * wave + i (256 bytes) of the stage with unit
+  // u = first_unit(wave) + i of the step, dwords 64 u + l (row d / 4, dword
+  // d % 4); slots past the wave's units_of(wave) repeat its first unit
+  // (loaded, never decoded).
+  uint32_t offA[kALoads], offW[kWpLoads];
+  auto set_loads = [&](int32_t it) {
+    const int32_t pos = start + it * nx;
+    const int32_t m0 = pos / a.tiles_c * BM, n0 = pos % a.tiles_c * BN;
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) {
+      const int r = 16 * (kALoads * wave + i) + (lane >> 2);
+      const int32_t m = m0 + r < a.M ? m0 + r : a.M - 1;
+      offA[i] = (uint32_t)(m * a.K + 16 * ((lane & 3) ^ ((r >> 1) & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < kWpLoads; ++i) {
+      // slot i of this wave holds unit first_unit + i, or repeats the first one
+      const int u = first_unit(wave) + (i < units_of(wave) ? i : 0);
+      const int r = 16 * u + (lane >> 2);
+      const int32_t n = n0 + r < a.N ? n0 + r : a.N - 1;
+      offW[i] = (uint32_t)(n * a.kb + 4 * (lane & 3));
+    }
+  };
+  // loads of step s (of the load tile) into stage st
+  auto issue = [&](int32_t st, int32_t s) {
+    const uint8_t *wb = a.Wp + 16 * s;
+    const uint32_t lw = lbase + kOffWp + st * kWpStage + wave * (kWpLoads * 256);
+#pragma unroll
+    for (int i = 0; i < kWpLoads; ++i) dma4(lw + 256 * i, offW[i], wb);
+    const int8_t *ab = a.A + 64 * s;
+    const uint32_t la = lbase + st * kAStage + wave * (kALoads * 1024);
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) dma16(la + 1024 * i, offA[i], ab);
+  };
+
+  v4i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v4i{0, 0, 0, 0};
+
+  // load cursor (tile it_ld, step s_ld): the next step whose loads go out;
+  // past the end it stays on the last step
+  int32_t it_ld = 0, s_ld = 0;
+  set_loads(0);
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) {
+    issue(p, s_ld);
+    if (s_ld + 1 < a.nk) {
+      ++s_ld;
+    } else if (it_ld + 1 < ntile) {
+      ++it_ld;
+      s_ld = 0;
+      set_loads(it_ld);
+    }
+  }
+  // prologue: steps 0 .. 2 have landed; decode 0 and 1; fragments of step 0
+  wait_vm<0>();
+  {
+    uint32_t x0[kWpLoads], x1[kWpLoads];
+    fs_decode_read(x0, smem + kOffWp, wave, lane);
+    fs_decode_read(x1, smem + kOffWp + kWpStage, wave, lane);
+    fs_decode_write(x0, smem + kOffWd, wave, lane);
+    fs_decode_write(x1, smem + kOffWd + kWdStage, wave, lane);
+  }
+  wait_barrier<0>();
+
+  const int frag = swz(lane & 15, lane >> 4);
+  const int qoff = wm * TM * LP + frag, poff = kOffWd + wn * TN * LP + frag;
+  // weight fragments stream through registers kPD ahead of their MFMAs,
+  // across step boundaries; the A fragments of a step stay for all of it
+  constexpr int kPD = 3;
+  static_assert(kPD < FN - FM, "prefetch distance");
+  v4i qc[FM], pf[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) qc[i] = *reinterpret_cast<const v4i *>(smem + qoff + i * 16 * LP);
+#pragma unroll
+  for (int jj = 0; jj < kPD; ++jj) pf[jj] = *reinterpret_cast<const v4i *>(smem + poff + jj * 16 * LP);
+
+  // Per step g: A stage g % 4 (a = g & 3), decoded stage g % 3 (d).  One
+  // step: loads of step g + 3 into stage (g + 3) % 4 = (a + 3) & 3, MFMAs of
+  // step g with the fragments of step g + 1 read alongside, the decode of
+  // step g + 2 into decoded stage (d + 2) % 3.
+  int32_t ga = 0, gd = 0;
+  bool after = false;  // a tile went out on the kStores path right before this step
+  for (int32_t it = 0; it < ntile; ++it) {
+    for (int32_t s = 0; s < a.nk; ++s) {
+      issue((ga + 3) & 3, s_ld);
+      if (s_ld + 1 < a.nk) {
+        ++s_ld;
+      } else if (it_ld + 1 < ntile) {
+        ++it_ld;
+        s_ld = 0;
+        set_loads(it_ld);
+      }
+
+      const int gd1 = gd == DS - 1 ? 0 : gd + 1, gd2 = gd1 == DS - 1 ? 0 : gd1 + 1;
+      const int8_t *pc = smem + poff + gd * kWdStage;
+      const int8_t *qn_ = smem + qoff + ((ga + 1) & 3) * kAStage;
+      const int8_t *pn_ = smem + poff + gd1 * kWdStage;
+      v4i qn[FM], pn[kPD];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) qn[i] = *reinterpret_cast<const v4i *>(qn_ + i * 16 * LP);
+      uint32_t x[kWpLoads];
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) {
+        if (jj + kPD < FN)
+          pf[jj + kPD] = *reinterpret_cast<const v4i *>(pc + (jj + kPD) * 16 * LP);
+        else
+          pn[jj + kPD - FN] = *reinterpret_cast<const v4i *>(pn_ + (jj + kPD - FN) * 16 * LP);
+        if (jj == FM) {
+          // this wave's packed codes of step g + 2 have landed: fetch them
+          if (after)
+            wait_vm<kWaitMid + kStores>();
+          else
+            wait_vm<kWaitMid>();
+          fs_decode_read(x, smem + kOffWp + ((ga + 2) & 3) * kWpStage, wave, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pf[jj], qc[i], acc[i][jj], 0, 0, 0);
+      }
+      fs_decode_write(x, smem + kOffWd + gd2 * kWdStage, wave, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) qc[i] = qn[i];
+#pragma unroll
+      for (int jj = 0; jj < kPD; ++jj) pf[jj] = pn[jj];
+
+      // end of step g: A(g + 2) has landed and decoded W(g + 2) is written.
+      // Stores issued right before this step are younger than A(g + 2);
+      // counting fewer operations than are younger is always safe.
+      if (after)
+        wait_barrier<kWaitEnd + kStores>();
+      else
+        wait_barrier<kWaitEnd>();
+      after = false;
+      ga = (ga + 1) & 3;
+      gd = gd1;
+    }
+
+    // the tile's output, on its way while the next tile's loads are in flight
+    const int32_t pos = start + it * nx;
+    const int32_t m0 = pos / a.tiles_c * BM, n0 = pos % a.tiles_c * BN;
+    const int32_t rb = m0 + wm * TM + (lane & 15);
+    const int32_t cb = n0 + wn * TN + (lane >> 4) * 4;
+    if (a.vec_out && m0 + BM <= a.M && n0 + BN <= a.N) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        int32_t *orow = a.C + (int64_t)(rb + 16 * i) * a.N + cb;
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) *reinterpret_cast<v4i *>(orow + 16 * jj) = acc[i][jj];
+      }
+      after = true;
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int32_t row = rb + 16 * i;
+        if (row >= a.M) continue;
+        int32_t *orow = a.C + (int64_t)row * a.N;
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+          const int32_t col = cb + 16 * jj;
+          if (a.vec_out && col + 3 < a.N) {
+            *reinterpret_cast<v4i *>(orow + col) = acc[i][jj];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < a.N) orow[col + e] = acc[i][jj][e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = v4i{0, 0, 0, 0};
+  }
+  // no transfer into LDS may outlive the workgroup
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -1029,7 +1361,31 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 // (A variant that loads the int8 operand of the forward and dX straight into
 // MFMA registers, without LDS, measured no faster in the three-product step
 // on MI355X and was left out.)
-enum KernelId { KTILED = 0, KSPLIT = 2 };
+enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3 };
+
+// The streaming forward kernel: applies when K is a whole number of steps,
+// the operands are aligned for its 16- and 4-byte loads, its 32-bit offsets
+// cannot overflow, and the output has enough tiles for a full persistent grid.
+constexpr int kStreamCUs = 256;  // MI355X compute units: one workgroup each
+
+struct StreamPlan {
+  bool ok;
+  int32_t tiles_r, tiles_c, tiles, grid;
+};
+
+StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, uintptr_t aalign, uintptr_t walign) {
+  StreamPlan sp{};
+  if (K % BK != 0 || aalign % 16 != 0 || walign % 4 != 0) return sp;
+  if (M > INT32_MAX / K || N > INT32_MAX / (K / 4)) return sp;
+  const int64_t tr = ceil_div(M, fs::BM), tc = ceil_div(N, fs::BN);
+  if (tr * tc < kStreamCUs) return sp;
+  sp.ok = true;
+  sp.tiles_r = (int32_t)tr;
+  sp.tiles_c = (int32_t)tc;
+  sp.tiles = (int32_t)(tr * tc);
+  sp.grid = kStreamCUs;
+  return sp;
+}
 
 int pick_kernel(int op, int tile, int64_t L) {
   if (op == DW && tile == TW && L >= 8 * BK) return KSPLIT;
@@ -1100,6 +1456,28 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
+  if (op == FWD) {
+    const StreamPlan sp = stream_plan(M, N, K, align_of(q), align_of(p));
+    if (sp.ok) {
+      SArgs sa;
+      sa.A = q;
+      sa.Wp = static_cast<const uint8_t *>(p);
+      sa.C = out;
+      sa.M = (int32_t)M;
+      sa.N = (int32_t)N;
+      sa.K = (int32_t)K;
+      sa.kb = (int32_t)(K / 4);
+      sa.tiles_r = sp.tiles_r;
+      sa.tiles_c = sp.tiles_c;
+      sa.band_cols = sp.tiles_c;
+      sa.tiles = sp.tiles;
+      sa.nk = (int32_t)(K / BK);
+      sa.vec_out = a.vec_out;
+      hipLaunchKernelGGL(tgemm_fwd_stream, dim3(sp.grid), dim3(fs::kNT), 0, stream, sa);
+      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+    }
+  }
+
   const int kernel = pick_kernel(op, tile, s.L);
   hipError_t e;
   if (op == FWD)
@@ -1151,33 +1529,69 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
-  const int tile = pick_tile(s);
-  const TileInfo &ti = kTileInfo[tile];
+  const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
   memset(plan, 0, sizeof(*plan));
   plan->out_rows = s.R;
   plan->out_cols = s.Cc;
   plan->contraction = s.L;
+  plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
+  if (op == FWD) {
+    const StreamPlan sp = stream_plan(M, N, K, al, al);
+    if (sp.ok) {
+      plan->tile_rows = fs::BM;
+      plan->tile_cols = fs::BN;
+      plan->tiles = sp.tiles;
+      plan->workgroups = sp.grid;
+      plan->tiles_per_workgroup = ceil_div(ceil_div(sp.tiles, 8), sp.grid / 8);
+      plan->band_cols = sp.tiles_c;
+      plan->kernel = KSTREAM;
+      plan->threads_per_workgroup = fs::kNT;
+      plan->lds_bytes = fs::kLds;
+      return TGEMM_OK;
+    }
+  }
+  const int tile = pick_tile(s);
+  const TileInfo &ti = kTileInfo[tile];
   plan->tile_rows = ti.bm;
   plan->tile_cols = ti.bn;
   plan->tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
   plan->workgroups = plan->tiles;
+  plan->tiles_per_workgroup = 1;
   plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
-  const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
-  plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   plan->kernel = pick_kernel(op, tile, s.L);
   plan->threads_per_workgroup = plan->kernel == KSPLIT ? 2 * kThreads : kThreads;
   plan->lds_bytes = kernel_lds(op, plan->kernel, tile);
   return TGEMM_OK;
 }
 
-int ternary_gemm_tile_of_block(const tgemm_plan *plan, int64_t block, int64_t *row0,
-                               int64_t *col0) {
+int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iteration, int64_t *row0,
+                         int64_t *col0) {
   if (!plan || !row0 || !col0) return TGEMM_ERR_NULL;
-  if (block < 0 || block >= plan->workgroups || plan->tiles > INT32_MAX) return TGEMM_ERR_DIM;
+  if (workgroup < 0 || workgroup >= plan->workgroups || iteration < 0 ||
+      iteration >= plan->tiles_per_workgroup || plan->tiles > INT32_MAX || plan->tile_rows < 1 ||
+      plan->tile_cols < 1)
+    return TGEMM_ERR_DIM;
   const int32_t tiles_c = (int32_t)ceil_div(plan->out_cols, plan->tile_cols);
+  const int32_t tiles = (int32_t)plan->tiles;
   int32_t tr, tc;
-  tile_rc(xcd_tile((int32_t)block, (int32_t)plan->tiles), (int32_t)(plan->tiles / tiles_c), tiles_c,
-          plan->band_cols, &tr, &tc);
+  if (plan->kernel == KSTREAM) {
+    // the kernel's own order: eight contiguous runs of row-major tile
+    // positions, one per XCD; workgroup b (XCD b % 8) takes every nx-th
+    // position of its run, starting at b / 8
+    if (plan->workgroups % 8 != 0) return TGEMM_ERR_DIM;
+    const int32_t nx = (int32_t)plan->workgroups / 8, xcd = (int32_t)(workgroup % 8);
+    const int32_t j = (int32_t)(workgroup / 8);
+    const int32_t q8 = tiles / 8, r8 = tiles % 8;
+    const int32_t start = xcd * q8 + (xcd < r8 ? xcd : r8);
+    const int32_t cnt = q8 + (xcd < r8 ? 1 : 0);
+    const int64_t pos = j + iteration * nx;
+    if (pos >= cnt) return TGEMM_ERR_DIM;
+    tr = (int32_t)((start + pos) / tiles_c);
+    tc = (int32_t)((start + pos) % tiles_c);
+  } else {
+    if (iteration != 0) return TGEMM_ERR_DIM;
+    tile_rc(xcd_tile((int32_t)workgroup, tiles), tiles / tiles_c, tiles_c, plan->band_cols, &tr, &tc);
+  }
   *row0 = (int64_t)tr * plan->tile_rows;
   *col0 = (int64_t)tc * plan->tile_cols;
   return TGEMM_OK;

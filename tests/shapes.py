@@ -25,3 +25,10 @@ DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
     (1088, 912, 4112), (1000, 901, 4101)]   # long contractions: the split dW kernel
 
 TILES = ((256, 128), (128, 144), (64, 64))
+
+# Shapes for the streaming forward kernel (K % 64 == 0, at least 256 tiles of
+# 256 x 288): interior tiles only, ragged M and N on both store paths (N % 4
+# != 0 has no 16-byte stores), tile counts that do not split evenly between
+# the workgroups, and one or two steps per tile.
+STREAM_SHAPES = [(16300, 3450, 640), (15000, 3460, 192), (4096, 4608, 64), (8192, 2304, 128),
+                 (40000, 1000, 2048)]

@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES, TILES
+from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES, STREAM_SHAPES, TILES
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -95,15 +95,21 @@ def test_alias_rejected():
 
 def _coverage(op, M, N, K):
     pl = B.plan(op, M, N, K)
-    seen = set()
-    for blk in range(pl.workgroups):
-        r0, c0 = B.tile_of_block(pl, blk)
-        assert r0 % pl.tile_rows == 0 and c0 % pl.tile_cols == 0
-        assert 0 <= r0 < pl.out_rows and 0 <= c0 < pl.out_cols
-        seen.add((r0, c0))
+    seen = []
+    for wg in range(pl.workgroups):
+        for it in range(pl.tiles_per_workgroup):
+            t = B.tile_of(pl, wg, it)
+            if t is None:
+                # a workgroup's tiles are a prefix of its iterations
+                assert all(B.tile_of(pl, wg, j) is None for j in range(it, pl.tiles_per_workgroup))
+                break
+            r0, c0 = t
+            assert r0 % pl.tile_rows == 0 and c0 % pl.tile_cols == 0
+            assert 0 <= r0 < pl.out_rows and 0 <= c0 < pl.out_cols
+            seen.append((r0, c0))
     want = {(r, c) for r in range(0, pl.out_rows, pl.tile_rows)
             for c in range(0, pl.out_cols, pl.tile_cols)}
-    assert seen == want and len(seen) == pl.workgroups
+    assert len(seen) == len(set(seen)) == pl.tiles and set(seen) == want
     return pl
 
 
@@ -111,22 +117,28 @@ def _coverage(op, M, N, K):
     ("fwd", 1, 16, 16), ("fwd", 300, 272, 96), ("fwd", 16384, 3456, 1280),
     ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
-    ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)])
+    ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
+    + [("fwd",) + s for s in STREAM_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
-    assert pl.threads_per_workgroup == (512 if pl.kernel == B.KERNEL_SPLIT else 256)
     assert pl.lds_bytes <= 160 * 1024
-    assert pl.workgroups == pl.tiles
+    if pl.kernel == B.KERNEL_STREAM:
+        assert pl.threads_per_workgroup == 512 and pl.workgroups == 256
+        per_xcd = -(-pl.tiles // 8)
+        assert pl.tiles_per_workgroup == -(-per_xcd // 32)
+    else:
+        assert pl.threads_per_workgroup == (512 if pl.kernel == B.KERNEL_SPLIT else 256)
+        assert pl.workgroups == pl.tiles and pl.tiles_per_workgroup == 1
 
 
 def test_parity_shapes_reach_every_tile_and_path():
     # the GPU parity shape lists exercise every tile shape on both load paths,
     # and every kernel on each load path it serves
-    kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1)},
+    kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
                "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
         for s in shapes:
             pl = B.plan(op, *s)
@@ -139,35 +151,62 @@ def test_parity_shapes_reach_every_tile_and_path():
 
 
 def test_kernel_choice():
-    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_TILED
+    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
+    assert B.plan("fwd", 16384, 3456, 1280, align=2).kernel == B.KERNEL_TILED   # A misaligned
+    assert B.plan("fwd", 16384, 3456, 1296).kernel == B.KERNEL_TILED    # K % 64 != 0
+    assert B.plan("fwd", 2048, 2048, 65536).kernel == B.KERNEL_TILED    # 64 tiles of 256 x 288
     assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_TILED
     assert B.plan("dw", 16384, 3456, 1280).kernel == B.KERNEL_SPLIT
     assert B.plan("dw", 80, 3904, 4112).kernel == B.KERNEL_TILED   # short contraction
     assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
+    for s in STREAM_SHAPES:
+        assert B.plan("fwd", *s).kernel == B.KERNEL_STREAM, s
 
 
-def test_block_out_of_range():
+def test_tile_query_out_of_range():
     pl = B.plan("fwd", 300, 272, 96)
     with pytest.raises(B.TernaryGemmError):
-        B.tile_of_block(pl, pl.workgroups)
+        B.tile_of(pl, pl.workgroups)
+    with pytest.raises(B.TernaryGemmError):
+        B.tile_of(pl, 0, 1)
+    pl = B.plan("fwd", 15000, 3460, 192)            # 767 tiles over 256 workgroups
+    assert B.tile_of(pl, 0, pl.tiles_per_workgroup - 1) is not None
+    assert sum(B.tile_of(pl, wg, pl.tiles_per_workgroup - 1) is None
+               for wg in range(pl.workgroups)) == 256 * pl.tiles_per_workgroup - 767
+
+
+def test_stream_schedule_mirror():
+    # a CPU mirror of the stream kernel's own schedule (written from its
+    # description: eight contiguous runs of row-major tile positions, workgroup
+    # b on run b % 8 taking every 32nd position from b / 8) gives the same tiles
+    pl = B.plan("fwd", 16300, 3450, 640)
+    tiles_c = -(-pl.out_cols // pl.tile_cols)
+    q, r = divmod(pl.tiles, 8)
+    for wg in range(pl.workgroups):
+        x, j = wg % 8, wg // 8
+        start, cnt = x * q + min(x, r), q + (x < r)
+        for it in range(pl.tiles_per_workgroup):
+            pos = j + it * 32
+            want = None if pos >= cnt else ((start + pos) // tiles_c * pl.tile_rows,
+                                            (start + pos) % tiles_c * pl.tile_cols)
+            assert B.tile_of(pl, wg, it) == want
 
 
 def test_same_xcd_tiles_share_rows():
-    # workgroups b and b+8 run on the same XCD; in the headline plan they take
-    # neighbouring tiles along the output columns of the same row panel
+    # workgroups on one XCD (b, b + 8, ...) work on neighbouring positions of
+    # one run at the same time: in the headline plan the tiles in flight on an
+    # XCD span at most four row panels
     pl = B.plan("fwd", 16384, 3456, 1280)
-    same_rows = 0
-    for b in range(0, 512):
-        r0, c0 = B.tile_of_block(pl, b)
-        r1, c1 = B.tile_of_block(pl, b + 8)
-        same_rows += (r0 == r1)
-    assert same_rows >= 0.9 * 512
+    for x in range(8):
+        for it in range(pl.tiles_per_workgroup):
+            rows = {B.tile_of(pl, wg, it)[0] for wg in range(x, pl.workgroups, 8)}
+            assert len(rows) <= 4, (x, it, rows)
 
 
 def test_headline_plan():
     pl = B.plan("fwd", 16384, 3456, 1280)
-    assert (pl.tile_rows, pl.tile_cols) == (256, 128)
-    assert pl.workgroups == 64 * 27
+    assert (pl.tile_rows, pl.tile_cols) == (256, 288)
+    assert pl.tiles == 64 * 12 and pl.workgroups == 256 and pl.tiles_per_workgroup == 3
     assert pl.fast_path == 1
     assert B.plan("fwd", 16384, 3456, 1280, align=2).fast_path == 0
     assert B.plan("fwd", 300, 272, 96).fast_path == 1        # 96 % 16 == 0
