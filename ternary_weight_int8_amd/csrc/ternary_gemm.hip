@@ -299,15 +299,17 @@ struct DecodeOp {
 // units.  With a power-of-two number of chunks per row, chunk c goes to slot
 // c ^ sw(m), sw mapping each such row set onto distinct 16-byte bank groups.
 // With an odd number (144-byte rows: 9), rows are packed and every second
-// block of 16 rows is shifted by 128 bytes, which does the same.  A model of
-// the 64 banks (checked for all four row lengths) and the counters on MI355X
-// both show no conflicts.
+// block of 16 rows is shifted by a further 128 bytes, which does the same;
+// with twice an odd number (160-byte rows: 10) the shift is 16 bytes.  A model of the 64 banks (checked for all five row
+// lengths) and the counters on MI355X both show no conflicts.
 template <int BT>
 struct RowLayout {
   static constexpr int kChunks = BT / 16;
   static_assert(BT % 16 == 0 && (BK * kChunks) % 64 == 0, "row length");
-  static_assert(kChunks == 4 || kChunks == 8 || kChunks == 16 || kChunks % 2 == 1, "row length");
+  static_assert(kChunks == 4 || kChunks == 8 || kChunks == 16 || kChunks % 2 == 1 || kChunks == 10,
+                "row length");
   static constexpr bool kOdd = kChunks % 2 == 1;
+  static constexpr bool kTwiceOdd = kChunks == 10;
   __host__ __device__ static constexpr int sw(int m) {
     return kChunks == 16  ? (m & 7) | (((m >> 4) & 1) << 3)
            : kChunks == 8 ? ((m >> 1) & 3) | (((m >> 4) & 1) << 2)
@@ -315,10 +317,10 @@ struct RowLayout {
                           : 0;
   }
   __host__ __device__ static constexpr int base(int m) {
-    return m * BT + (kOdd ? 128 * (((m >> 4) + 1) >> 1) : 0);
+    return m * BT + (kOdd ? 128 : kTwiceOdd ? 16 : 0) * (((m >> 4) + 1) >> 1);
   }
   __host__ __device__ static constexpr int at(int m, int c) { return base(m) + 16 * (c ^ sw(m)); }
-  static constexpr int kBytes = BK * BT + (kOdd ? 256 : 0);  // one stage
+  static constexpr int kBytes = BK * BT + (kOdd ? 256 : kTwiceOdd ? 32 : 0);  // one stage
 };
 
 template <int BT, bool FAST>
@@ -1010,77 +1012,111 @@ void tgemm_dw_split(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming forward kernel (large outputs, K % 64 == 0, aligned operands).
+// Streaming kernels: forward and dX on large outputs.
 //
-// One workgroup of 8 waves per CU, persistent over its tiles of 256 x 288
-// outputs (16384 x 3456 splits into 768 such tiles: three per CU).  The waves
-// form a 4 x 2 grid of 64 x 144 sub-tiles, two waves per SIMD.
+// One workgroup of 8 waves per CU, persistent over its tiles of 512 output
+// rows x BN output columns (forward 16384 x 3456: 768 tiles of 512 x 144,
+// three per CU; dX 16384 x 1280: 256 tiles of 512 x 160, one per CU).  The
+// waves are stacked 8 x 1, each a 64 x BN sub-tile, two waves per SIMD; the
+// tall tile spreads each decoded weight over 512 rows, which halves the
+// decode work per MAC of a 256-row tile.
 //
-// Staging goes straight from global memory into LDS (never through VGPRs):
-// A rows with 16-byte loads and packed weight rows with 4-byte loads, issued
-// S - 1 steps ahead into a ring of S stages.  Each wave decodes the packed
-// dwords it loaded itself (16 codes -> one 16-byte chunk, the table lookup
-// of decode16) into a ring of three decoded stages, two steps ahead, so the
+// The row operand Q (A for the forward, dC for dX: rows of the output, along
+// the contraction) and the packed weight rows go straight from global memory
+// into LDS (never through VGPRs): Q with 16-byte loads into a ring of three
+// stages, packed codes with 4-byte loads into a ring of two.  Each wave
+// decodes the packed dwords it loaded itself (16 codes -> a 16-byte chunk,
+// decode16) into a ring of three decoded stages, two steps ahead, so the
 // codes are decoded once per tile load [P10425 "What this adds"] and the
 // decode needs only the wave's own load count, no extra barrier.
+//   forward: decoded stage = rows n of the tile, 64 codes of k each (swz
+//            layout), read as fragments with 16-byte LDS reads;
+//   dX:      decoded stage = rows n of the contraction, BN codes of k each
+//            (RowLayout), read as fragments with the transposing LDS read
+//            (TrRead), as the packed rows of W lie along k [P10855 PR body].
 //
-// Register pipeline: during the MFMAs of step g a wave reads the A fragments
-// and the first weight fragment of step g + 1 (A fragments stay in registers
-// for the whole step; weight fragments stream through, one ahead), so the
-// MFMA issue never waits for LDS at a step boundary.  Hence the barrier that
-// starts step g publishes A(g + 1) and decoded W(g + 1).
+// Register pipeline: during the MFMAs of step g a wave reads the Q fragments
+// and the first weight fragments of step g + 1 (Q fragments stay in
+// registers for the whole step; weight fragments stream through, kPD ahead),
+// so the MFMA issue does not wait for LDS at a step boundary.  The barrier
+// that starts step g therefore publishes Q(g + 1) and decoded W(g + 1), and a
+// Q stage is free once the step before its own has read it: three stages
+// keep the loads two steps ahead.
 //
 // The loads come from inline assembly, so the compiler does not drain them
 // at every LDS read; each wave waits for its own loads with explicit vmcnt
 // counts (memory operations of a wave complete in issue order, so vmcnt(N),
 // N = the operations issued after the awaited one, is exactly that wait):
 //
-//   step g  top:  issue batch B(g + 3) = packed W then A of step g + 3
-//           mid:  wait for the packed W of step g + 2, decode it
-//           end:  wait for A(g + 2); barrier
+//   step g  cols 0 .. 4: issue batch B(g + 3) = packed W, then Q, of step g + 3
+//           col 5:  wait for the packed W of step g + 2, fetch it for decoding
+//           end:    decode it; wait for Q(g + 2); barrier
 //
-// A tile's output is stored right after its last step, while loads of the
-// next tile are in flight; its kStores stores are younger than what the next
-// three waits await, and those waits count them.  The last steps re-load
-// the final step (valid addresses, never used), which keeps the counts
-// uniform; the kernel waits for every load before it ends, so no transfer
-// into LDS outlives it.
+// The loads of a step are spread over the MFMA columns so that the eight
+// waves do not queue them all at once behind the barrier.  A tile's output is
+// stored right after its last step, while loads of the next tile are in
+// flight; its kStores stores are younger than what the next two waits await,
+// and those waits count them.  The last steps re-load the final step (valid
+// addresses, never used), which keeps the counts uniform; the kernel waits
+// for every load before it ends, so no transfer into LDS outlives it.
 // ---------------------------------------------------------------------------
 namespace fs {
 
-constexpr int BM = 256, BN = 288, S = 4;          // tile, LDS stages of loads
+constexpr int S = 3;                              // Q stages
 constexpr int DS = 3;                             // decoded weight stages
+constexpr int PS = 2;                             // packed weight stages
 constexpr int kWaves = 8, kNT = 64 * kWaves;
-constexpr int WN = 2, TM = 64, TN = 144;          // wave grid 4 x 2
-constexpr int FM = TM / 16, FN = TN / 16;
-constexpr int kAStage = BM * LP;                  // A rows of one step
-constexpr int kWdStage = BN * LP;                 // decoded weights of one step
+constexpr int BM = 512, TM = 64, FM = TM / 16;    // 8 x 1 waves of 64 rows
+constexpr int kAStage = BM * LP;                  // Q rows of one step
 constexpr int kALoads = kAStage / 1024 / kWaves;  // 16-byte loads per wave per step
-constexpr int kWpLoads = 3;                       // 4-byte loads per wave per step
-constexpr int kWpStage = kWaves * kWpLoads * 256; // packed rows (BN * 16 used)
-constexpr int kWpUnits = BN * 16 / 256;           // 4-byte loads that carry codes
-// Units (and so their decode) per wave: q or q + 1, the extra ones on the
-// last waves; waves w and w + 4 share a SIMD, so per-SIMD decode work differs
-// by at most one unit.
-constexpr int kUnitQ = kWpUnits / kWaves, kUnitR = kWpUnits % kWaves;
-__host__ __device__ constexpr int units_of(int w) { return kUnitQ + (w >= kWaves - kUnitR ? 1 : 0); }
-__host__ __device__ constexpr int first_unit(int w) {
-  return kUnitQ * w + (w > kWaves - kUnitR ? w - (kWaves - kUnitR) : 0);
-}
-constexpr int kOffWd = S * kAStage;
-constexpr int kOffWp = kOffWd + DS * kWdStage;
-constexpr int kLds = kOffWp + S * kWpStage;
-constexpr int kBatch = kALoads + kWpLoads;
-constexpr int kStores = FM * FN;
-constexpr int kWaitMid = kALoads + kBatch;        // A(g + 2), B(g + 3)
-constexpr int kWaitEnd = kBatch;                  // B(g + 3)
-static_assert(BM == TM * (kWaves / WN) && BN == TN * WN, "wave grid");
-static_assert(kALoads * kWaves * 1024 == kAStage, "A stage = whole 1 KB wave loads");
-static_assert(BN * 16 % 256 == 0 && kUnitQ + (kUnitR ? 1 : 0) <= kWpLoads, "packed stage");
-static_assert(first_unit(kWaves - 1) + units_of(kWaves - 1) == kWpUnits, "units");
-static_assert(kLds <= 160 * 1024, "LDS");
-static_assert(S == 4 && kWaitMid + kStores <= 63, "vmcnt field");
-static_assert(FN > FM, "A fragments of the next step are read during the first FM columns");
+constexpr int kPD = 3;                            // weight fragments read ahead
+
+template <int OP>
+struct Geo;
+
+template <int OP>
+struct GeoBase {
+  static constexpr int BN = OP == FWD ? 144 : 160;
+  static constexpr int FN = BN / 16;
+  // forward: decoded rows n of the tile (swz layout); dX: decoded rows = the
+  // step's 64 contraction indices n, BN bytes each (RowLayout)
+  static constexpr int kWdStage = OP == FWD ? BN * LP : RowLayout<BN>::kBytes;
+  // packed dwords of one step: forward BN rows x 4 (64 codes of k); dX 64
+  // rows x BN / 16 (BN codes of k); in units of one 64-lane load
+  static constexpr int kDwPerRow = OP == FWD ? BK / 16 : BN / 16;
+  static constexpr int kUnits = (OP == FWD ? BN * BK / 16 : BK * BN / 16) / 64;
+  // Units (loads and their decode) per wave: q or q + 1, the extra ones on
+  // the last waves; waves w and w + 4 share a SIMD, so per-SIMD decode work
+  // differs by at most one unit.
+  static constexpr int kUnitQ = kUnits / kWaves, kUnitR = kUnits % kWaves;
+  static constexpr int kWpLoads = kUnitQ + (kUnitR ? 1 : 0);
+  __host__ __device__ static constexpr int units_of(int w) {
+    return kUnitQ + (w >= kWaves - kUnitR ? 1 : 0);
+  }
+  __host__ __device__ static constexpr int first_unit(int w) {
+    return kUnitQ * w + (w > kWaves - kUnitR ? w - (kWaves - kUnitR) : 0);
+  }
+  static constexpr int kWpStage = kUnits * 256;   // unit u at byte 256 u
+  static constexpr int kOffWd = S * kAStage;
+  static constexpr int kOffWp = kOffWd + DS * kWdStage;
+  static constexpr int kLds = kOffWp + PS * kWpStage;
+  static constexpr int kBatch = kALoads + kUnitQ; // loads of a step, fewest over the waves
+  static constexpr int kStores = FM * FN;
+  // Waits count the operations issued after the awaited one; a wave with an
+  // extra unit has one more, and counting fewer than there are is safe.
+  static constexpr int kWaitMid = kALoads + kBatch;  // own packed W(g + 2): Q(g + 2), B(g + 3) after it
+  static constexpr int kWaitEnd = kBatch;            // own Q(g + 2): B(g + 3) after it
+  static_assert(kALoads * kWaves * 1024 == kAStage, "Q stage = whole 1 KB wave loads");
+  static_assert(kUnits * 64 * 4 == (OP == FWD ? BN * 16 : BK * BN / 4) && kUnitQ >= 1, "packed stage");
+  static_assert(first_unit(kWaves - 1) + units_of(kWaves - 1) == kUnits, "units");
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(kWaitMid + kStores <= 63, "vmcnt field");
+  static_assert(kPD < FN - FM && kALoads + 1 < FN, "prefetch distance, load columns");
+};
+template <>
+struct Geo<FWD> : GeoBase<FWD> {};
+template <>
+struct Geo<DX> : GeoBase<DX> {};
 
 // 16 bytes per lane from sbase + voff into LDS at lds + 16 * lane
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *sbase) {
@@ -1106,12 +1142,14 @@ __device__ __forceinline__ void wait_barrier() {
 }  // namespace fs
 
 struct SArgs {
-  const int8_t *A;
-  const uint8_t *Wp;
-  int32_t *C;
-  int32_t M, N, K, kb;          // kb = K / 4, the packed row stride
-  int32_t tiles_r, tiles_c, band_cols, tiles;
-  int32_t nk;                   // steps per tile (K / 64)
+  const int8_t *Q;    // A (forward) or dC (dX): rows of the output along the contraction
+  const uint8_t *Wp;  // packed weights
+  int32_t *out;
+  int32_t R, Cc, L;   // output rows, output columns, contraction
+  int32_t ldq;        // Q row stride (= L)
+  int32_t kb;         // packed row stride (K / 4)
+  int32_t tiles_c, tiles;
+  int32_t nk;         // L / 64
   int32_t vec_out;
 };
 
@@ -1119,39 +1157,45 @@ struct SArgs {
 // can go out well before their results are used: fs_decode_read fetches the
 // dwords (16 codes each), fs_decode_write turns each into a 16-byte chunk of
 // int8 weights (decode16) and stores it in the decoded stage.
-__device__ __forceinline__ void fs_decode_read(uint32_t (&x)[fs::kWpLoads], const int8_t *src, int wave,
-                                               int lane) {
-  using namespace fs;
+template <int OP>
+__device__ __forceinline__ void fs_decode_read(uint32_t (&x)[fs::Geo<OP>::kWpLoads], const int8_t *src,
+                                               int wave, int lane) {
+  typedef fs::Geo<OP> G;
 #pragma unroll
-  for (int i = 0; i < kWpLoads; ++i)
-    if (i < units_of(wave))
-      x[i] = *reinterpret_cast<const uint32_t *>(src + 256 * (kWpLoads * wave + i) + 4 * lane);
+  for (int i = 0; i < G::kWpLoads; ++i)
+    if (i < G::units_of(wave))
+      x[i] = *reinterpret_cast<const uint32_t *>(src + 256 * (G::first_unit(wave) + i) + 4 * lane);
 }
-__device__ __forceinline__ void fs_decode_write(const uint32_t (&x)[fs::kWpLoads], int8_t *dst, int wave,
-                                                int lane) {
-  using namespace fs;
+template <int OP>
+__device__ __forceinline__ void fs_decode_write(const uint32_t (&x)[fs::Geo<OP>::kWpLoads], int8_t *dst,
+                                                int wave, int lane) {
+  typedef fs::Geo<OP> G;
 #pragma unroll
-  for (int i = 0; i < kWpLoads; ++i)
-    if (i < units_of(wave)) {
-      const int d = 64 * (first_unit(wave) + i) + lane;  // packed dword of the step: row d / 4
-      *reinterpret_cast<v4i *>(dst + swz(d >> 2, d & 3)) = decode16(x[i]);
+  for (int i = 0; i < G::kWpLoads; ++i)
+    if (i < G::units_of(wave)) {
+      const int d = 64 * (G::first_unit(wave) + i) + lane;  // packed dword of the step
+      const int off = OP == FWD ? swz(d >> 2, d & 3)        // row n = d / 4, 16 codes of k
+                                : RowLayout<G::BN>::at(d / G::kDwPerRow, d % G::kDwPerRow);
+      *reinterpret_cast<v4i *>(dst + off) = decode16(x[i]);
     }
 }
 
+template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(fs::kNT, fs::kNT), amdgpu_waves_per_eu(2)))
-void tgemm_fwd_stream(SArgs a) {
+void tgemm_stream(SArgs a) {
   using namespace fs;
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kLds];
+  typedef Geo<OP> G;
+  constexpr int BN = G::BN, FN = G::FN;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[G::kLds];
   const uint32_t lbase = (uint32_t)(uintptr_t)smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
 
   // Tiles of this workgroup: the tile positions (row-major over the tile
   // grid) are split into eight contiguous runs, one per XCD (workgroup b runs
   // on XCD b % 8), and the nx workgroups of an XCD take every nx-th position
-  // of its run, so the tiles an XCD works on at one time share A rows and
-  // the weight columns in its L2.
+  // of its run, so the tiles an XCD works on at one time share Q rows and the
+  // weight columns in its L2.
   const int32_t nx = (int32_t)gridDim.x / 8, xcd = (int32_t)blockIdx.x % 8, j0 = (int32_t)blockIdx.x / 8;
   const int32_t q8 = a.tiles / 8, r8 = a.tiles % 8;
   const int32_t start = xcd * q8 + (xcd < r8 ? xcd : r8) + j0;
@@ -1159,42 +1203,50 @@ void tgemm_fwd_stream(SArgs a) {
   const int32_t ntile = cnt > j0 ? (cnt - j0 + nx - 1) / nx : 0;
   if (ntile == 0) return;
 
-  // Load offsets of a tile.  A load i of this wave fills tile rows
-  // 16 L .. 16 L + 15 (L = kALoads * wave + i); lane l lands in slot l % 4 of
-  // row 16 L + l / 4 and so fetches the chunk the swizzle puts there.  Packed
-  // load i fills slot kWpLoads * wave + i (256 bytes) of the stage with unit
-  // u = first_unit(wave) + i of the step, dwords 64 u + l (row d / 4, dword
-  // d % 4); slots past the wave's units_of(wave) repeat its first unit
-  // (loaded, never decoded).
-  uint32_t offA[kALoads], offW[kWpLoads];
+  // Load offsets of a tile (recomputed per tile, not kept live across the
+  // loop).  Q load i of this wave fills tile rows 16 L .. 16 L + 15 (L =
+  // kALoads * wave + i); lane l lands in slot l % 4 of row 16 L + l / 4 and so
+  // fetches the chunk the swizzle puts there.  Packed load i (i <
+  // units_of(wave)) fills unit u = first_unit(wave) + i of the step, 256
+  // bytes at 256 u of the packed stage: dwords d = 64 u + l.  Forward: row
+  // d / 4 of the tile's columns, dword d % 4 of the step's 16 bytes.  dX:
+  // contraction row d / kDwPerRow of the step, dword d % kDwPerRow of the
+  // tile's BN / 4 bytes.  Rows and columns past the output load a valid
+  // neighbour (computed, never stored).
+  uint32_t offA[kALoads], offW[G::kWpLoads];
   auto set_loads = [&](int32_t it) {
     const int32_t pos = start + it * nx;
     const int32_t m0 = pos / a.tiles_c * BM, n0 = pos % a.tiles_c * BN;
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
       const int r = 16 * (kALoads * wave + i) + (lane >> 2);
-      const int32_t m = m0 + r < a.M ? m0 + r : a.M - 1;
-      offA[i] = (uint32_t)(m * a.K + 16 * ((lane & 3) ^ ((r >> 1) & 3)));
+      const int32_t m = m0 + r < a.R ? m0 + r : a.R - 1;
+      offA[i] = (uint32_t)(m * a.ldq + 16 * ((lane & 3) ^ ((r >> 1) & 3)));
     }
 #pragma unroll
-    for (int i = 0; i < kWpLoads; ++i) {
-      // slot i of this wave holds unit first_unit + i, or repeats the first one
-      const int u = first_unit(wave) + (i < units_of(wave) ? i : 0);
-      const int r = 16 * u + (lane >> 2);
-      const int32_t n = n0 + r < a.N ? n0 + r : a.N - 1;
-      offW[i] = (uint32_t)(n * a.kb + 4 * (lane & 3));
+    for (int i = 0; i < G::kWpLoads; ++i) {
+      const int d = 64 * (G::first_unit(wave) + (i < G::units_of(wave) ? i : 0)) + lane;
+      if constexpr (OP == FWD) {
+        const int32_t n = n0 + (d >> 2) < a.Cc ? n0 + (d >> 2) : a.Cc - 1;
+        offW[i] = (uint32_t)(n * a.kb + 4 * (d & 3));
+      } else {
+        const int32_t kw = n0 / 4 + 4 * (d % G::kDwPerRow);
+        offW[i] = (uint32_t)((d / G::kDwPerRow) * a.kb + (kw + 4 <= a.kb ? kw : a.kb - 4));
+      }
     }
   };
-  // loads of step s (of the load tile) into stage st
-  auto issue = [&](int32_t st, int32_t s) {
-    const uint8_t *wb = a.Wp + 16 * s;
-    const uint32_t lw = lbase + kOffWp + st * kWpStage + wave * (kWpLoads * 256);
+  // packed-code and Q base addresses of step s of the load tile
+  auto wbase = [&](int32_t s) {
+    return OP == FWD ? a.Wp + 16 * s : a.Wp + (int64_t)BK * s * a.kb;
+  };
+  auto issue = [&](int32_t st, int32_t ps, int32_t s) {
+    const uint32_t lw = lbase + G::kOffWp + ps * G::kWpStage + 256 * G::first_unit(wave);
 #pragma unroll
-    for (int i = 0; i < kWpLoads; ++i) dma4(lw + 256 * i, offW[i], wb);
-    const int8_t *ab = a.A + 64 * s;
+    for (int i = 0; i < G::kWpLoads; ++i)
+      if (i < G::units_of(wave)) dma4(lw + 256 * i, offW[i], wbase(s));
     const uint32_t la = lbase + st * kAStage + wave * (kALoads * 1024);
 #pragma unroll
-    for (int i = 0; i < kALoads; ++i) dma16(la + 1024 * i, offA[i], ab);
+    for (int i = 0; i < kALoads; ++i) dma16(la + 1024 * i, offA[i], a.Q + 64 * s);
   };
 
   v4i acc[FM][FN];
@@ -1206,10 +1258,7 @@ void tgemm_fwd_stream(SArgs a) {
   // load cursor (tile it_ld, step s_ld): the next step whose loads go out;
   // past the end it stays on the last step
   int32_t it_ld = 0, s_ld = 0;
-  set_loads(0);
-#pragma unroll
-  for (int p = 0; p < S - 1; ++p) {
-    issue(p, s_ld);
+  auto next_load = [&]() {
     if (s_ld + 1 < a.nk) {
       ++s_ld;
     } else if (it_ld + 1 < ntile) {
@@ -1217,100 +1266,124 @@ void tgemm_fwd_stream(SArgs a) {
       s_ld = 0;
       set_loads(it_ld);
     }
-  }
-  // prologue: steps 0 .. 2 have landed; decode 0 and 1; fragments of step 0
+  };
+  set_loads(0);
+  // prologue: steps 0 and 1 land and are decoded (each wave its own units,
+  // whose loads it has waited for), then step 2 goes out into packed stage 0
+  issue(0, 0, s_ld);
+  next_load();
+  issue(1, 1, s_ld);
+  next_load();
   wait_vm<0>();
   {
-    uint32_t x0[kWpLoads], x1[kWpLoads];
-    fs_decode_read(x0, smem + kOffWp, wave, lane);
-    fs_decode_read(x1, smem + kOffWp + kWpStage, wave, lane);
-    fs_decode_write(x0, smem + kOffWd, wave, lane);
-    fs_decode_write(x1, smem + kOffWd + kWdStage, wave, lane);
+    uint32_t x0[G::kWpLoads], x1[G::kWpLoads];
+    fs_decode_read<OP>(x0, smem + G::kOffWp, wave, lane);
+    fs_decode_read<OP>(x1, smem + G::kOffWp + G::kWpStage, wave, lane);
+    fs_decode_write<OP>(x0, smem + G::kOffWd, wave, lane);
+    fs_decode_write<OP>(x1, smem + G::kOffWd + G::kWdStage, wave, lane);
   }
-  wait_barrier<0>();
+  issue(2, 0, s_ld);
+  next_load();
+  wait_barrier<G::kBatch>();
 
-  const int frag = swz(lane & 15, lane >> 4);
-  const int qoff = wm * TM * LP + frag, poff = kOffWd + wn * TN * LP + frag;
-  // weight fragments stream through registers kPD ahead of their MFMAs,
-  // across step boundaries; the A fragments of a step stay for all of it
-  constexpr int kPD = 3;
-  static_assert(kPD < FN - FM, "prefetch distance");
+  // fragment offsets: Q rows of this wave (swz layout); weight fragment jj of
+  // a decoded stage at poff + jj * pstep
+  const int qoff = wave * TM * LP + swz(lane & 15, lane >> 4);
+  const int poff = G::kOffWd + (OP == FWD ? swz(lane & 15, lane >> 4) : TrRead::off<RowLayout<BN>>(0, lane));
+  constexpr int pstep = OP == FWD ? 16 * LP : 16;
+  auto pfrag = [&](const int8_t *p) -> v4i {
+    if constexpr (OP == FWD)
+      return *reinterpret_cast<const v4i *>(p);
+    else
+      return TrRead::frag(p, 8 * BN);
+  };
+
   v4i qc[FM], pf[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) qc[i] = *reinterpret_cast<const v4i *>(smem + qoff + i * 16 * LP);
 #pragma unroll
-  for (int jj = 0; jj < kPD; ++jj) pf[jj] = *reinterpret_cast<const v4i *>(smem + poff + jj * 16 * LP);
+  for (int jj = 0; jj < kPD; ++jj) pf[jj] = pfrag(smem + poff + jj * pstep);
+  // every wave's reads of Q stage 0 are done before step 0 loads into it
+  wait_barrier<G::kBatch>();
 
-  // Per step g: A stage g % 4 (a = g & 3), decoded stage g % 3 (d).  One
-  // step: loads of step g + 3 into stage (g + 3) % 4 = (a + 3) & 3, MFMAs of
-  // step g with the fragments of step g + 1 read alongside, the decode of
-  // step g + 2 into decoded stage (d + 2) % 3.
-  int32_t ga = 0, gd = 0;
+  // Per step g: stage index t = g % 3 of the Q and decoded rings, g % 2 of the
+  // packed ring.  Step g loads step g + 3 into Q stage t (read as step g's
+  // fragments during step g - 1) and packed stage (g + 1) % 2 (whose codes
+  // this wave decoded in step g - 1), computes step g from decoded stage t
+  // with Q fragments already in registers, reads step g + 1's fragments from
+  // stages t + 1, and decodes step g + 2 from packed stage g % 2 into decoded
+  // stage t + 2.
+  int32_t gt = 0, gp = 0;
   bool after = false;  // a tile went out on the kStores path right before this step
   for (int32_t it = 0; it < ntile; ++it) {
     for (int32_t s = 0; s < a.nk; ++s) {
-      issue((ga + 3) & 3, s_ld);
-      if (s_ld + 1 < a.nk) {
-        ++s_ld;
-      } else if (it_ld + 1 < ntile) {
-        ++it_ld;
-        s_ld = 0;
-        set_loads(it_ld);
-      }
-
-      const int gd1 = gd == DS - 1 ? 0 : gd + 1, gd2 = gd1 == DS - 1 ? 0 : gd1 + 1;
-      const int8_t *pc = smem + poff + gd * kWdStage;
-      const int8_t *qn_ = smem + qoff + ((ga + 1) & 3) * kAStage;
-      const int8_t *pn_ = smem + poff + gd1 * kWdStage;
+      const int t1 = gt == 2 ? 0 : gt + 1, t2 = t1 == 2 ? 0 : t1 + 1;
+      const uint32_t lw3 = lbase + G::kOffWp + (gp ^ 1) * G::kWpStage + 256 * G::first_unit(wave);
+      const uint32_t la3 = lbase + gt * kAStage + wave * (kALoads * 1024);
+      const uint8_t *wb3 = wbase(s_ld);
+      const int8_t *ab3 = a.Q + 64 * s_ld;
+      const int8_t *pc = smem + poff + gt * G::kWdStage;
+      const int8_t *pn_ = smem + poff + t1 * G::kWdStage;
+      const int8_t *qn_ = smem + qoff + t1 * kAStage;
       v4i qn[FM], pn[kPD];
 #pragma unroll
       for (int i = 0; i < FM; ++i) qn[i] = *reinterpret_cast<const v4i *>(qn_ + i * 16 * LP);
-      uint32_t x[kWpLoads];
+      uint32_t x[G::kWpLoads];
 #pragma unroll
       for (int jj = 0; jj < FN; ++jj) {
+        // loads of step g + 3, spread over the columns: packed codes at
+        // column 0, Q load i at column 1 + i
+        if (jj == 0) {
+#pragma unroll
+          for (int i = 0; i < G::kWpLoads; ++i)
+            if (i < G::units_of(wave)) dma4(lw3 + 256 * i, offW[i], wb3);
+        }
+        if (jj >= 1 && jj <= kALoads) dma16(la3 + 1024 * (jj - 1), offA[jj - 1], ab3);
         if (jj + kPD < FN)
-          pf[jj + kPD] = *reinterpret_cast<const v4i *>(pc + (jj + kPD) * 16 * LP);
+          pf[jj + kPD] = pfrag(pc + (jj + kPD) * pstep);
         else
-          pn[jj + kPD - FN] = *reinterpret_cast<const v4i *>(pn_ + (jj + kPD - FN) * 16 * LP);
-        if (jj == FM) {
-          // this wave's packed codes of step g + 2 have landed: fetch them
+          pn[jj + kPD - FN] = pfrag(pn_ + (jj + kPD - FN) * pstep);
+        if (jj == kALoads + 1) {
+          // every load of step g + 3 is out; this wave's packed codes of step
+          // g + 2 have landed: fetch them
           if (after)
-            wait_vm<kWaitMid + kStores>();
+            wait_vm<G::kWaitMid + G::kStores>();
           else
-            wait_vm<kWaitMid>();
-          fs_decode_read(x, smem + kOffWp + ((ga + 2) & 3) * kWpStage, wave, lane);
+            wait_vm<G::kWaitMid>();
+          fs_decode_read<OP>(x, smem + G::kOffWp + gp * G::kWpStage, wave, lane);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           acc[i][jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pf[jj], qc[i], acc[i][jj], 0, 0, 0);
       }
-      fs_decode_write(x, smem + kOffWd + gd2 * kWdStage, wave, lane);
+      fs_decode_write<OP>(x, smem + G::kOffWd + t2 * G::kWdStage, wave, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i) qc[i] = qn[i];
 #pragma unroll
       for (int jj = 0; jj < kPD; ++jj) pf[jj] = pn[jj];
+      next_load();
 
-      // end of step g: A(g + 2) has landed and decoded W(g + 2) is written.
-      // Stores issued right before this step are younger than A(g + 2);
+      // end of step g: Q(g + 2) has landed and decoded W(g + 2) is written.
+      // Stores issued right before this step are younger than Q(g + 2);
       // counting fewer operations than are younger is always safe.
       if (after)
-        wait_barrier<kWaitEnd + kStores>();
+        wait_barrier<G::kWaitEnd + G::kStores>();
       else
-        wait_barrier<kWaitEnd>();
+        wait_barrier<G::kWaitEnd>();
       after = false;
-      ga = (ga + 1) & 3;
-      gd = gd1;
+      gt = t1;
+      gp ^= 1;
     }
 
     // the tile's output, on its way while the next tile's loads are in flight
     const int32_t pos = start + it * nx;
     const int32_t m0 = pos / a.tiles_c * BM, n0 = pos % a.tiles_c * BN;
-    const int32_t rb = m0 + wm * TM + (lane & 15);
-    const int32_t cb = n0 + wn * TN + (lane >> 4) * 4;
-    if (a.vec_out && m0 + BM <= a.M && n0 + BN <= a.N) {
+    const int32_t rb = m0 + wave * TM + (lane & 15);
+    const int32_t cb = n0 + (lane >> 4) * 4;
+    if (a.vec_out && m0 + BM <= a.R && n0 + BN <= a.Cc) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int32_t *orow = a.C + (int64_t)(rb + 16 * i) * a.N + cb;
+        int32_t *orow = a.out + (int64_t)(rb + 16 * i) * a.Cc + cb;
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) *reinterpret_cast<v4i *>(orow + 16 * jj) = acc[i][jj];
       }
@@ -1319,17 +1392,17 @@ void tgemm_fwd_stream(SArgs a) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int32_t row = rb + 16 * i;
-        if (row >= a.M) continue;
-        int32_t *orow = a.C + (int64_t)row * a.N;
+        if (row >= a.R) continue;
+        int32_t *orow = a.out + (int64_t)row * a.Cc;
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
           const int32_t col = cb + 16 * jj;
-          if (a.vec_out && col + 3 < a.N) {
+          if (a.vec_out && col + 3 < a.Cc) {
             *reinterpret_cast<v4i *>(orow + col) = acc[i][jj];
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (col + e < a.N) orow[col + e] = acc[i][jj][e];
+              if (col + e < a.Cc) orow[col + e] = acc[i][jj][e];
           }
         }
       }
@@ -1363,21 +1436,26 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 // on MI355X and was left out.)
 enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3 };
 
-// The streaming forward kernel: applies when K is a whole number of steps,
-// the operands are aligned for its 16- and 4-byte loads, its 32-bit offsets
+// The streaming kernels (forward, dX): apply when the contraction is a whole
+// number of steps, the operands are aligned for their 16- and 4-byte loads
+// (dX: packed columns in whole dwords, K % 16 == 0), their 32-bit offsets
 // cannot overflow, and the output has enough tiles for a full persistent grid.
 constexpr int kStreamCUs = 256;  // MI355X compute units: one workgroup each
 
 struct StreamPlan {
   bool ok;
-  int32_t tiles_r, tiles_c, tiles, grid;
+  int32_t bn, tiles_r, tiles_c, tiles, grid, lds;
 };
 
-StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, uintptr_t aalign, uintptr_t walign) {
+StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
   StreamPlan sp{};
-  if (K % BK != 0 || aalign % 16 != 0 || walign % 4 != 0) return sp;
-  if (M > INT32_MAX / K || N > INT32_MAX / (K / 4)) return sp;
-  const int64_t tr = ceil_div(M, fs::BM), tc = ceil_div(N, fs::BN);
+  if (op == DW || qalign % 16 != 0 || walign % 4 != 0) return sp;
+  const Shape s = shape_of(op, M, N, K);
+  if (s.L % BK != 0 || (op == DX && K % 16 != 0)) return sp;
+  if (M > INT32_MAX / s.L || N > INT32_MAX / (K / 4) || s.R > INT32_MAX / s.Cc) return sp;
+  sp.bn = op == FWD ? fs::Geo<FWD>::BN : fs::Geo<DX>::BN;
+  sp.lds = op == FWD ? fs::Geo<FWD>::kLds : fs::Geo<DX>::kLds;
+  const int64_t tr = ceil_div(s.R, fs::BM), tc = ceil_div(s.Cc, sp.bn);
   if (tr * tc < kStreamCUs) return sp;
   sp.ok = true;
   sp.tiles_r = (int32_t)tr;
@@ -1456,24 +1534,26 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
-  if (op == FWD) {
-    const StreamPlan sp = stream_plan(M, N, K, align_of(q), align_of(p));
+  {
+    const StreamPlan sp = stream_plan(op, M, N, K, align_of(q), align_of(p));
     if (sp.ok) {
       SArgs sa;
-      sa.A = q;
+      sa.Q = q;
       sa.Wp = static_cast<const uint8_t *>(p);
-      sa.C = out;
-      sa.M = (int32_t)M;
-      sa.N = (int32_t)N;
-      sa.K = (int32_t)K;
+      sa.out = out;
+      sa.R = (int32_t)s.R;
+      sa.Cc = (int32_t)s.Cc;
+      sa.L = (int32_t)s.L;
+      sa.ldq = (int32_t)s.L;
       sa.kb = (int32_t)(K / 4);
-      sa.tiles_r = sp.tiles_r;
       sa.tiles_c = sp.tiles_c;
-      sa.band_cols = sp.tiles_c;
       sa.tiles = sp.tiles;
-      sa.nk = (int32_t)(K / BK);
+      sa.nk = (int32_t)(s.L / BK);
       sa.vec_out = a.vec_out;
-      hipLaunchKernelGGL(tgemm_fwd_stream, dim3(sp.grid), dim3(fs::kNT), 0, stream, sa);
+      if (op == FWD)
+        hipLaunchKernelGGL(tgemm_stream<FWD>, dim3(sp.grid), dim3(fs::kNT), 0, stream, sa);
+      else
+        hipLaunchKernelGGL(tgemm_stream<DX>, dim3(sp.grid), dim3(fs::kNT), 0, stream, sa);
       return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
     }
   }
@@ -1535,18 +1615,18 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->out_cols = s.Cc;
   plan->contraction = s.L;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
-  if (op == FWD) {
-    const StreamPlan sp = stream_plan(M, N, K, al, al);
+  {
+    const StreamPlan sp = stream_plan(op, M, N, K, al, al);
     if (sp.ok) {
       plan->tile_rows = fs::BM;
-      plan->tile_cols = fs::BN;
+      plan->tile_cols = sp.bn;
       plan->tiles = sp.tiles;
       plan->workgroups = sp.grid;
       plan->tiles_per_workgroup = ceil_div(ceil_div(sp.tiles, 8), sp.grid / 8);
       plan->band_cols = sp.tiles_c;
       plan->kernel = KSTREAM;
       plan->threads_per_workgroup = fs::kNT;
-      plan->lds_bytes = fs::kLds;
+      plan->lds_bytes = sp.lds;
       return TGEMM_OK;
     }
   }

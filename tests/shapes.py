@@ -27,8 +27,13 @@ DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
 TILES = ((256, 128), (128, 144), (64, 64))
 
 # Shapes for the streaming forward kernel (K % 64 == 0, at least 256 tiles of
-# 256 x 288): interior tiles only, ragged M and N on both store paths (N % 4
+# 512 x 144): interior tiles only, ragged M and N on both store paths (N % 4
 # != 0 has no 16-byte stores), tile counts that do not split evenly between
 # the workgroups, and one or two steps per tile.
 STREAM_SHAPES = [(16300, 3450, 640), (15000, 3460, 192), (4096, 4608, 64), (8192, 2304, 128),
                  (40000, 1000, 2048)]
+
+# Shapes for the streaming dX kernel (contraction N % 64 == 0, K % 16 == 0, at
+# least 256 tiles of 512 x 160): the timed shape, ragged M with a last column
+# tile of 16 or 144 of its 160 columns, and one or two contraction steps.
+DX_STREAM_SHAPES = [(16300, 3456, 1296), (15000, 2048, 1424), (8192, 64, 5120), (4096, 128, 10240)]

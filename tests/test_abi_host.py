@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES, STREAM_SHAPES, TILES
+from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, STREAM_SHAPES, TILES
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -118,7 +118,7 @@ def _coverage(op, M, N, K):
     ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
-    + [("fwd",) + s for s in STREAM_SHAPES])
+    + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.lds_bytes <= 160 * 1024
@@ -135,10 +135,11 @@ def test_parity_shapes_reach_every_tile_and_path():
     # the GPU parity shape lists exercise every tile shape on both load paths,
     # and every kernel on each load path it serves
     kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
-               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1)},
+               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES), ("dx", DX_SHAPES), ("dw", DW_SHAPES)):
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES), ("dx", DX_SHAPES + DX_STREAM_SHAPES),
+                       ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
         for s in shapes:
             pl = B.plan(op, *s)
@@ -154,8 +155,13 @@ def test_kernel_choice():
     assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
     assert B.plan("fwd", 16384, 3456, 1280, align=2).kernel == B.KERNEL_TILED   # A misaligned
     assert B.plan("fwd", 16384, 3456, 1296).kernel == B.KERNEL_TILED    # K % 64 != 0
-    assert B.plan("fwd", 2048, 2048, 65536).kernel == B.KERNEL_TILED    # 64 tiles of 256 x 288
-    assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_TILED
+    assert B.plan("fwd", 2048, 2048, 65536).kernel == B.KERNEL_TILED    # 60 tiles of 512 x 144
+    assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
+    assert B.plan("dx", 16384, 3456, 1288).kernel == B.KERNEL_TILED    # K % 16 != 0
+    assert B.plan("dx", 16384, 3400, 1280).kernel == B.KERNEL_TILED    # N % 64 != 0
+    assert B.plan("dx", 1782, 3456, 1280).kernel == B.KERNEL_TILED     # 32 tiles of 512 x 160
+    for s in DX_STREAM_SHAPES:
+        assert B.plan("dx", *s).kernel == B.KERNEL_STREAM, s
     assert B.plan("dw", 16384, 3456, 1280).kernel == B.KERNEL_SPLIT
     assert B.plan("dw", 80, 3904, 4112).kernel == B.KERNEL_TILED   # short contraction
     assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
@@ -169,10 +175,11 @@ def test_tile_query_out_of_range():
         B.tile_of(pl, pl.workgroups)
     with pytest.raises(B.TernaryGemmError):
         B.tile_of(pl, 0, 1)
-    pl = B.plan("fwd", 15000, 3460, 192)            # 767 tiles over 256 workgroups
+    pl = B.plan("fwd", 15000, 3460, 192)            # 750 tiles over 256 workgroups
+    assert pl.tiles == 750 and pl.tiles_per_workgroup == 3
     assert B.tile_of(pl, 0, pl.tiles_per_workgroup - 1) is not None
     assert sum(B.tile_of(pl, wg, pl.tiles_per_workgroup - 1) is None
-               for wg in range(pl.workgroups)) == 256 * pl.tiles_per_workgroup - 767
+               for wg in range(pl.workgroups)) == 256 * pl.tiles_per_workgroup - 750
 
 
 def test_stream_schedule_mirror():
@@ -205,7 +212,7 @@ def test_same_xcd_tiles_share_rows():
 
 def test_headline_plan():
     pl = B.plan("fwd", 16384, 3456, 1280)
-    assert (pl.tile_rows, pl.tile_cols) == (256, 288)
+    assert (pl.tile_rows, pl.tile_cols) == (512, 144)
     assert pl.tiles == 64 * 12 and pl.workgroups == 256 and pl.tiles_per_workgroup == 3
     assert pl.fast_path == 1
     assert B.plan("fwd", 16384, 3456, 1280, align=2).fast_path == 0

@@ -14,7 +14,7 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
-from shapes import DW_SHAPES, DX_SHAPES, FWD_SHAPES, STREAM_SHAPES
+from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, STREAM_SHAPES
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -165,6 +165,13 @@ def test_fwd_stream_shapes(M, N, K):
     say(f"fwd stream {M}x{N}x{K} plan={tile_of('fwd', M, N, K)}")
     A, Wp = synth.fwd_inputs(M * 11 + K, M, N, K, 4)
     assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd stream {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", DX_STREAM_SHAPES)
+def test_dx_stream_shapes(M, N, K):
+    say(f"dx stream {M}x{N}x{K} plan={tile_of('dx', M, N, K)}")
+    dC, Wp = synth.dx_inputs(M * 13 + N, M, N, K, 4)
+    assert_exact(gpu_dx(dC, Wp, K), oracle.dx(dC, Wp, K), f"dx stream {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", DX_SHAPES)
