@@ -124,11 +124,13 @@ const char *ternary_gemm_status_str(int status);
 #define TGEMM_KERNEL_TILED 0   /* one 4-wave workgroup per output tile          */
 #define TGEMM_KERNEL_SPLIT 2   /* dW: the tile's contraction split between two
                                   4-wave halves of one workgroup              */
-#define TGEMM_KERNEL_STREAM 3  /* forward, K % 64 == 0, 16-byte aligned A and
-                                  4-byte aligned Wpacked, M*K and N*K/4 below
-                                  2^31, at least 256 tiles of 256 x 288: one
-                                  persistent 8-wave workgroup per CU, operands
-                                  loaded straight into LDS                    */
+#define TGEMM_KERNEL_STREAM 3  /* forward (K % 64 == 0) and dX (N % 64 == 0,
+                                  K % 16 == 0) on 16-byte aligned A or dC and
+                                  4-byte aligned Wpacked, 32-bit offsets, at
+                                  least 256 tiles of 512 x 144 (forward) or
+                                  512 x 160 (dX): one persistent 8-wave
+                                  workgroup per CU, operands loaded straight
+                                  into LDS                                    */
 
 typedef struct tgemm_plan {
     int64_t out_rows, out_cols, contraction;
