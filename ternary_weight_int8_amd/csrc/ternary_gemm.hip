@@ -1381,11 +1381,23 @@ void tgemm_stream(SArgs a) {
     const int32_t rb = m0 + wave * TM + (lane & 15);
     const int32_t cb = n0 + (lane >> 4) * 4;
     if (a.vec_out && m0 + BM <= a.R && n0 + BN <= a.Cc) {
+      // Lane l of a fragment holds row l % 16, so neighbouring lanes hit
+      // different rows and a CU's stores drain at a third of the rate of
+      // row-contiguous ones.  A lane permutation (ds_bpermute, no LDS memory)
+      // first moves row L / 4, columns 4 (L % 4) .. + 3 to lane L: four
+      // neighbouring lanes then write one 64-byte run.
+      const int src = 4 * ((lane >> 2) + 16 * (lane & 3));
+      const int32_t rp = m0 + wave * TM + (lane >> 2), cp = n0 + (lane & 3) * 4;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int32_t *orow = a.out + (int64_t)(rb + 16 * i) * a.Cc + cb;
+        int32_t *orow = a.out + (int64_t)(rp + 16 * i) * a.Cc + cp;
 #pragma unroll
-        for (int jj = 0; jj < FN; ++jj) *reinterpret_cast<v4i *>(orow + 16 * jj) = acc[i][jj];
+        for (int jj = 0; jj < FN; ++jj) {
+          v4i v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_ds_bpermute(src, acc[i][jj][e]);
+          *reinterpret_cast<v4i *>(orow + 16 * jj) = v;
+        }
       }
       after = true;
     } else {
