@@ -55,7 +55,9 @@ typedef enum tgemm_status {
     TGEMM_ERR_PACK = -3,   /* the packed dimension K is not a multiple of 4     */
     TGEMM_ERR_BOUND = -4,  /* the contraction is longer than the exact-int32 bound */
     TGEMM_ERR_ALIAS = -5,  /* the output overlaps an input                       */
-    TGEMM_ERR_HIP = -6     /* the HIP runtime reported an error at launch        */
+    TGEMM_ERR_HIP = -6,    /* the HIP runtime reported an error at launch        */
+    TGEMM_ERR_KIND = -7    /* the output kind of a scaled call is not one of
+                              TGEMM_OUT_F32, TGEMM_OUT_BF16                    */
 } tgemm_status;
 
 /* Longest contraction for which every int32 result is exact whatever the
@@ -103,6 +105,47 @@ int ternary_gemm_s8_dx(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX,
  */
 int ternary_gemm_s8_dw(const int8_t *A, const int8_t *dC, int32_t *dW,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Scaled outputs: the integer product followed by its dequantization, fused
+ * into the kernels' stores.  The pages leave the scales to the host: the
+ * activations are quantized per row for dX and X and dY per column for dW
+ * [P10855 PR body]; the forward takes the same per-row activation scale, and
+ * the ternary weights one scale for the whole matrix (the reading taken).
+ * Each output element is
+ *     y = (float(acc) * row_scale[row]) * col_scale
+ * where acc is the exact int32 result of the plain call, the int32 -> float
+ * conversion and each product are IEEE single precision rounded to nearest
+ * even, in that order, and col_scale is the weight scale (forward, dX) or
+ * dc_col_scale[n] (dW).  TGEMM_OUT_F32 stores y as float; TGEMM_OUT_BF16
+ * stores y rounded to the nearest bfloat16, ties to even (a NaN stays a
+ * quiet NaN), as uint16 bit patterns, which halves the bytes written.
+ * Scale vectors are DEVICE float arrays; output element counts and layouts
+ * are those of the plain calls.  Besides the plain calls' checks, a NULL
+ * scale vector returns TGEMM_ERR_NULL, an output kind other than the two
+ * below TGEMM_ERR_KIND, and an output overlapping a scale vector
+ * TGEMM_ERR_ALIAS.
+ */
+#define TGEMM_OUT_F32 1
+#define TGEMM_OUT_BF16 2
+
+/* forward: Y[m][n] = (float(C[m][n]) * a_row_scale[m]) * w_scale;
+ * a_row_scale float [M]. */
+int ternary_gemm_s8_scaled(const int8_t *A, const uint8_t *Wpacked, const float *a_row_scale,
+                           float w_scale, void *Y, int out_kind,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* dX: Y[m][k] = (float(dX[m][k]) * dc_row_scale[m]) * w_scale;
+ * dc_row_scale float [M]. */
+int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const float *dc_row_scale,
+                              float w_scale, void *dX, int out_kind,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* dW: Y[k][n] = (float(dW[k][n]) * a_col_scale[k]) * dc_col_scale[n];
+ * a_col_scale float [K], dc_col_scale float [N]. */
+int ternary_gemm_s8_dw_scaled(const int8_t *A, const int8_t *dC, const float *a_col_scale,
+                              const float *dc_col_scale, void *dW, int out_kind,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *ternary_gemm_status_str(int status);

@@ -158,3 +158,63 @@ def dw(A, dC, threads=None, allow_overflow=False, return_overflows=False):
     dW = np.empty((K, N), dtype=np.int32)
     dW, r = _run("oracle_dw", A, dC, dW, M, N, K, threads, allow_overflow)
     return (dW, r) if return_overflows else dW
+
+
+# ---------------------------------------------------------------------------
+# Scaled outputs: the dequantization that follows the integer product.  The
+# pages leave the scales to the host (activations per row for dX, X and dY
+# per column for dW [P10855 PR body]); the reading taken is
+#     y = (float32(acc) * row_scale[row]) * col_scale[col]
+# in IEEE single precision, each step rounded to nearest even, in that order,
+# then optionally rounded to the nearest bfloat16, ties to even.
+# ---------------------------------------------------------------------------
+
+def bf16_value(bits) -> np.ndarray:
+    """float64 value of bfloat16 bit patterns (uint16), finite or not: an
+    all-ones exponent is taken as the next power of two past the largest
+    finite value (2^128), the value that rounding to bf16 overflows to."""
+    b = np.asarray(bits, dtype=np.uint32)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = ((b >> 7) & 0xFF).astype(np.int64)
+    m = (b & 0x7F).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -133), np.ldexp(128.0 + m, (e - 134).astype(np.int64)))
+    return sign * mag
+
+
+def bf16_nearest_even(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 values: the nearest bf16,
+    ties to the one with an even last mantissa bit; +-inf stay inf, values at
+    or past the midpoint above the largest finite bf16 become inf, and a NaN
+    becomes a quiet NaN with the same sign and top payload bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lo = (u >> 16) & 0xFFFF                        # toward zero
+    hi = lo + 1                                    # away from zero (same sign)
+    xv = x.astype(np.float64)
+    d_lo = np.abs(xv - bf16_value(lo))
+    d_hi = np.abs(bf16_value(hi) - xv)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & 1) == 1))
+    out = np.where(pick_hi, hi, lo)
+    out = np.where(np.isinf(x), lo, out)
+    out = np.where(np.isnan(x), lo | 0x40, out)
+    return out.astype(np.uint16)
+
+
+def scale_output(acc, row_scale, col_scale, out: str) -> np.ndarray:
+    """Scaled output of an integer result acc [R][C]: row_scale float32 [R],
+    col_scale float32 [C] or one float32 for every column; out "f32" gives
+    float32 [R][C], "bf16" the bfloat16 bit patterns as uint16 [R][C]."""
+    acc = np.asarray(acc)
+    if acc.dtype != np.int32:
+        raise TypeError("acc must be int32")
+    rs = np.asarray(row_scale, dtype=np.float32)
+    assert rs.shape == (acc.shape[0],)
+    y = acc.astype(np.float32) * rs[:, None]
+    cs = np.asarray(col_scale, dtype=np.float32)
+    y = y * (cs[None, :] if cs.ndim else cs)
+    assert y.dtype == np.float32
+    if out == "f32":
+        return y
+    if out == "bf16":
+        return bf16_nearest_even(y)
+    raise ValueError(f"out must be 'f32' or 'bf16', got {out!r}")

@@ -12,7 +12,8 @@ import os
 from .build import LIB
 
 OK = 0
-ERR_NULL, ERR_DIM, ERR_PACK, ERR_BOUND, ERR_ALIAS, ERR_HIP = -1, -2, -3, -4, -5, -6
+ERR_NULL, ERR_DIM, ERR_PACK, ERR_BOUND, ERR_ALIAS, ERR_HIP, ERR_KIND = -1, -2, -3, -4, -5, -6, -7
+OUT_F32, OUT_BF16 = 1, 2   # output kinds of the scaled calls
 
 # entry points declared in include/ternary_gemm.h
 EXPORTS = (
@@ -22,6 +23,9 @@ EXPORTS = (
     "ternary_gemm_status_str",
     "ternary_gemm_plan",
     "ternary_gemm_tile_of",
+    "ternary_gemm_s8_scaled",
+    "ternary_gemm_s8_dx_scaled",
+    "ternary_gemm_s8_dw_scaled",
 )
 
 OPS = {"fwd": 0, "dx": 1, "dw": 2}
@@ -72,6 +76,13 @@ def lib():
         L.ternary_gemm_tile_of.argtypes = [ctypes.POINTER(TgemmPlan), i64, i64,
                                            ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.ternary_gemm_tile_of.restype = ctypes.c_int
+        f32, i32 = ctypes.c_float, ctypes.c_int
+        for name in ("ternary_gemm_s8_scaled", "ternary_gemm_s8_dx_scaled"):
+            f = getattr(L, name)
+            f.argtypes = [p, p, p, f32, p, i32, i64, i64, i64, p]
+            f.restype = ctypes.c_int
+        L.ternary_gemm_s8_dw_scaled.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
+        L.ternary_gemm_s8_dw_scaled.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -83,6 +94,12 @@ def status_str(status: int) -> str:
 def call_raw(name: str, p0, p1, p2, M: int, N: int, K: int, stream=None) -> int:
     """Call an entry point with raw addresses (ints or None); returns its status."""
     return getattr(lib(), name)(p0, p1, p2, M, N, K, stream)
+
+
+def call_raw_scaled(name: str, p0, p1, s0, s1, out, kind: int, M: int, N: int, K: int, stream=None) -> int:
+    """Call a scaled entry point with raw addresses; s1 is the weight scale
+    (a float) for the forward and dX, the dC column scales' address for dW."""
+    return getattr(lib(), name)(p0, p1, s0, s1, out, kind, M, N, K, stream)
 
 
 def plan(op: str, M: int, N: int, K: int, align: int = 256):
@@ -190,3 +207,95 @@ def ternary_gemm_s8_dw(A, dC, dW=None, stream=None):
     if tuple(dW.shape) != (K, N):
         raise ValueError(f"dW must be [{K}][{N}]")
     return _invoke("ternary_gemm_s8_dw", A, dC, dW, M, N, K, stream)
+
+
+# ---------------------------------------------------------------------------
+# scaled outputs: the integer product times per-row and per-column scales,
+# stored as float32 or bfloat16
+# ---------------------------------------------------------------------------
+
+def _out_kind(dtype):
+    torch = _torch()
+    if dtype == torch.float32:
+        return OUT_F32
+    if dtype == torch.bfloat16:
+        return OUT_BF16
+    raise TypeError(f"out_dtype must be torch.float32 or torch.bfloat16, got {dtype}")
+
+
+def _scales(t, n, what):
+    torch = _torch()
+    _check(t, torch.float32, 1, what)
+    if t.shape[0] != n:
+        raise ValueError(f"{what} must have {n} entries, got {t.shape[0]}")
+
+
+def _output(out, shape, dtype, device, what):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=device)
+    _check(out, dtype, 2, what)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"{what} must be {list(shape)}")
+    return out
+
+
+def ternary_gemm_s8_scaled(A, Wpacked, a_row_scale, w_scale, out_dtype=None, Y=None, stream=None):
+    """Y [M][N] = (float(A x W) * a_row_scale[m]) * w_scale, float32 or bfloat16."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _check(A, torch.int8, 2, "A")
+    _check(Wpacked, torch.uint8, 2, "Wpacked")
+    M, K = A.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 4 != K:
+        raise ValueError(f"Wpacked must be [N][K/4] = [{N}][{K // 4}], got {tuple(Wpacked.shape)}")
+    _scales(a_row_scale, M, "a_row_scale")
+    Y = _output(Y, (M, N), out_dtype, A.device, "Y")
+    st = lib().ternary_gemm_s8_scaled(A.data_ptr(), Wpacked.data_ptr(), a_row_scale.data_ptr(),
+                                      float(w_scale), Y.data_ptr(), _out_kind(out_dtype), M, N, K,
+                                      _stream(stream, Y.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_scaled", st, status_str(st))
+    return Y
+
+
+def ternary_gemm_s8_dx_scaled(dC, Wpacked, K, dc_row_scale, w_scale, out_dtype=None, dX=None,
+                              stream=None):
+    """dX [M][K] = (float(dC x W^T) * dc_row_scale[m]) * w_scale, float32 or bfloat16."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _check(dC, torch.int8, 2, "dC")
+    _check(Wpacked, torch.uint8, 2, "Wpacked")
+    M, N = dC.shape
+    if tuple(Wpacked.shape) != (N, K // 4) or K % 4:
+        raise ValueError(f"Wpacked must be [N][K/4] = [{N}][{K // 4}], got {tuple(Wpacked.shape)}")
+    _scales(dc_row_scale, M, "dc_row_scale")
+    dX = _output(dX, (M, K), out_dtype, dC.device, "dX")
+    st = lib().ternary_gemm_s8_dx_scaled(dC.data_ptr(), Wpacked.data_ptr(), dc_row_scale.data_ptr(),
+                                         float(w_scale), dX.data_ptr(), _out_kind(out_dtype), M, N, K,
+                                         _stream(stream, dX.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_dx_scaled", st, status_str(st))
+    return dX
+
+
+def ternary_gemm_s8_dw_scaled(A, dC, a_col_scale, dc_col_scale, out_dtype=None, dW=None, stream=None):
+    """dW [K][N] = (float(A^T x dC) * a_col_scale[k]) * dc_col_scale[n], float32 or bfloat16."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _check(A, torch.int8, 2, "A")
+    _check(dC, torch.int8, 2, "dC")
+    M, K = A.shape
+    if dC.shape[0] != M:
+        raise ValueError("A and dC must have the same number of rows")
+    N = dC.shape[1]
+    _scales(a_col_scale, K, "a_col_scale")
+    _scales(dc_col_scale, N, "dc_col_scale")
+    dW = _output(dW, (K, N), out_dtype, A.device, "dW")
+    st = lib().ternary_gemm_s8_dw_scaled(A.data_ptr(), dC.data_ptr(), a_col_scale.data_ptr(),
+                                         dc_col_scale.data_ptr(), dW.data_ptr(), _out_kind(out_dtype),
+                                         M, N, K, _stream(stream, dW.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_dw_scaled", st, status_str(st))
+    return dW

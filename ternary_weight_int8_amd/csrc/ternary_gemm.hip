@@ -90,16 +90,83 @@ struct Flag {
 };
 
 
+// ---------------------------------------------------------------------------
+// The output of a call: the int32 sums as computed, or the sums scaled into
+// f32 or bf16 (the dequantization step that follows the integer product:
+// activations quantized per row for the forward and dX, X and dY per column
+// for dW [P10855 PR body]).  A scaled element is
+//     y = (float(acc) * rs[row]) * cs[col]          (cs null: cscal)
+// with the int32 -> float conversion and each product rounded to nearest-even
+// in IEEE single precision, in that order; bf16 output then rounds y to the
+// nearest bf16, ties to even (v_cvt_pk_bf16_f32; a NaN stays a NaN).
+// ---------------------------------------------------------------------------
+enum OutKind { OUT_I32 = 0, OUT_F32 = TGEMM_OUT_F32, OUT_BF16 = TGEMM_OUT_BF16 };
+static_assert(OUT_F32 != OUT_I32 && OUT_BF16 != OUT_I32 && OUT_F32 != OUT_BF16, "output kinds");
+
+struct Out {
+  void *ptr;          // [R][Cc] elements of the kind
+  const float *rs;    // per output row (scaled kinds)
+  const float *cs;    // per output column, or null: cscal for every column
+  float cscal;
+  int32_t kind;       // OutKind
+  int32_t vec;        // Cc % 4 == 0 and ptr aligned to 4 elements: 4-element stores
+  int32_t vec8;       // bf16, Cc % 8 == 0 and ptr 16-byte aligned: 8-element stores
+};
+
+__device__ __forceinline__ float scaled(int32_t x, float r, float c) {
+  return __fmul_rn(__fmul_rn((float)x, r), c);
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) packed low, high
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// columns col .. col + 3 of row `row`, all inside the output (o.vec); r is
+// the row's scale (read by the caller; unused for int32)
+__device__ __forceinline__ void put4(const Out &o, int64_t Cc, int64_t row, int64_t col, const v4i &v, float r) {
+  const int64_t e = row * Cc + col;
+  if (o.kind == OUT_I32) {
+    *reinterpret_cast<v4i *>(static_cast<int32_t *>(o.ptr) + e) = v;
+    return;
+  }
+  float y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) y[k] = scaled(v[k], r, o.cs ? o.cs[col + k] : o.cscal);
+  if (o.kind == OUT_F32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(o.ptr) + e) = make_float4(y[0], y[1], y[2], y[3]);
+  } else {
+    uint2 b;
+    b.x = bf16_pack(y[0], y[1]);
+    b.y = bf16_pack(y[2], y[3]);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(o.ptr) + e) = b;
+  }
+}
+__device__ __forceinline__ void put1(const Out &o, int64_t Cc, int64_t row, int64_t col, int32_t x, float r) {
+  const int64_t e = row * Cc + col;
+  if (o.kind == OUT_I32) {
+    static_cast<int32_t *>(o.ptr)[e] = x;
+    return;
+  }
+  const float y = scaled(x, r, o.cs ? o.cs[col] : o.cscal);
+  if (o.kind == OUT_F32)
+    static_cast<float *>(o.ptr)[e] = y;
+  else
+    static_cast<uint16_t *>(o.ptr)[e] = __builtin_bit_cast(uint16_t, (__bf16)y);
+}
+__device__ __forceinline__ float row_scale(const Out &o, int64_t row) {
+  return o.kind == OUT_I32 ? 0.f : o.rs[row];
+}
+
 struct Args {
   const int8_t *q;    // Q source
   const void *p;      // P source (Wpacked for FWD/DX, dC for DW)
-  int32_t *out;
+  Out o;
   int64_t R, Cc, L;   // output rows, output cols, contraction length
   int64_t ldq, ldp;   // row strides (bytes) of the Q and P sources
   int32_t tiles_c;    // column tiles
   int32_t band_cols;  // tile columns per band of the workgroup -> tile order
   int32_t tiles;      // total tiles (= workgroups)
-  int32_t vec_out;    // Cc % 4 == 0 and out 16-B aligned: 16-B stores
 };
 
 // ---------------------------------------------------------------------------
@@ -672,12 +739,13 @@ __device__ __forceinline__ void store_tile(const Args &a, const v4i (&acc)[T::FM
                                            int64_t c0, bool inside, int lane) {
   const int64_t rbase = r0 + (lane & 15);
   const int64_t cbase = c0 + (lane >> 4) * 4;
-  if (a.vec_out && inside) {
+  if (a.o.vec && inside) {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-      int32_t *orow = a.out + (rbase + i * 16) * a.Cc + cbase;
+      const int64_t row = rbase + i * 16;
+      const float r = row_scale(a.o, row);
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) *reinterpret_cast<v4i *>(orow + j * 16) = acc[i][j];
+      for (int j = 0; j < T::FN; ++j) put4(a.o, a.Cc, row, cbase + j * 16, acc[i][j], r);
     }
     return;
   }
@@ -685,16 +753,16 @@ __device__ __forceinline__ void store_tile(const Args &a, const v4i (&acc)[T::FM
   for (int i = 0; i < T::FM; ++i) {
     const int64_t row = rbase + i * 16;
     if (row >= a.R) continue;
-    int32_t *orow = a.out + row * a.Cc;
+    const float r = row_scale(a.o, row);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
       const int64_t col = cbase + j * 16;
-      if (a.vec_out && col + 3 < a.Cc) {
-        *reinterpret_cast<v4i *>(orow + col) = acc[i][j];
+      if (a.o.vec && col + 3 < a.Cc) {
+        put4(a.o, a.Cc, row, col, acc[i][j], r);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (col + e < a.Cc) orow[col + e] = acc[i][j][e];
+          if (col + e < a.Cc) put1(a.o, a.Cc, row, col + e, acc[i][j][e], r);
       }
     }
   }
@@ -1102,6 +1170,7 @@ struct GeoBase {
   static constexpr int kLds = kOffWp + PS * kWpStage;
   static constexpr int kBatch = kALoads + kUnitQ; // loads of a step, fewest over the waves
   static constexpr int kStores = FM * FN;
+  static constexpr int kStoresPair = FM * (FN / 2 + FN % 2);   // bf16 stores of fragment pairs
   // Waits count the operations issued after the awaited one; a wave with an
   // extra unit has one more, and counting fewer than there are is safe.
   static constexpr int kWaitMid = kALoads + kBatch;  // own packed W(g + 2): Q(g + 2), B(g + 3) after it
@@ -1144,13 +1213,12 @@ __device__ __forceinline__ void wait_barrier() {
 struct SArgs {
   const int8_t *Q;    // A (forward) or dC (dX): rows of the output along the contraction
   const uint8_t *Wp;  // packed weights
-  int32_t *out;
+  Out o;              // column scale, when scaled: o.cscal (o.cs is null)
   int32_t R, Cc, L;   // output rows, output columns, contraction
   int32_t ldq;        // Q row stride (= L)
   int32_t kb;         // packed row stride (K / 4)
   int32_t tiles_c, tiles;
   int32_t nk;         // L / 64
-  int32_t vec_out;
 };
 
 // The decode of a wave's own packed dwords, in two halves so that the reads
@@ -1187,6 +1255,11 @@ void tgemm_stream(SArgs a) {
   typedef Geo<OP> G;
   constexpr int BN = G::BN, FN = G::FN;
   __shared__ __attribute__((aligned(1024))) int8_t smem[G::kLds];
+  // row scales of the tile (scaled output): each wave loads those of its own
+  // 64 rows straight into LDS at the tile's first step, and reads them back
+  // when it stores the tile
+  __shared__ __attribute__((aligned(256))) float rs_s[BM];
+  const bool scaled_out = a.o.kind != OUT_I32;
   const uint32_t lbase = (uint32_t)(uintptr_t)smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1314,7 +1387,9 @@ void tgemm_stream(SArgs a) {
   // stages t + 1, and decodes step g + 2 from packed stage g % 2 into decoded
   // stage t + 2.
   int32_t gt = 0, gp = 0;
-  bool after = false;  // a tile went out on the kStores path right before this step
+  // stores a tile's vector path issued right before this step: 0, or
+  // kStoresPair (bf16 in fragment pairs), or kStores
+  int after = 0;
   for (int32_t it = 0; it < ntile; ++it) {
     for (int32_t s = 0; s < a.nk; ++s) {
       const int t1 = gt == 2 ? 0 : gt + 1, t2 = t1 == 2 ? 0 : t1 + 1;
@@ -1325,6 +1400,12 @@ void tgemm_stream(SArgs a) {
       const int8_t *pc = smem + poff + gt * G::kWdStage;
       const int8_t *pn_ = smem + poff + t1 * G::kWdStage;
       const int8_t *qn_ = smem + qoff + t1 * kAStage;
+      if (scaled_out && s == 0) {
+        // this wave's row scales of tile it: older than the loads this step
+        // issues below, so landed once step 1 has waited for those
+        const int32_t m = (start + it * nx) / a.tiles_c * BM + wave * TM + lane;
+        dma4((uint32_t)(uintptr_t)rs_s + 4 * TM * wave, 4 * (uint32_t)(m < a.R ? m : a.R - 1), a.o.rs);
+      }
       v4i qn[FM], pn[kPD];
 #pragma unroll
       for (int i = 0; i < FM; ++i) qn[i] = *reinterpret_cast<const v4i *>(qn_ + i * 16 * LP);
@@ -1346,8 +1427,10 @@ void tgemm_stream(SArgs a) {
         if (jj == kALoads + 1) {
           // every load of step g + 3 is out; this wave's packed codes of step
           // g + 2 have landed: fetch them
-          if (after)
+          if (after == G::kStores)
             wait_vm<G::kWaitMid + G::kStores>();
+          else if (after == G::kStoresPair)
+            wait_vm<G::kWaitMid + G::kStoresPair>();
           else
             wait_vm<G::kWaitMid>();
           fs_decode_read<OP>(x, smem + G::kOffWp + gp * G::kWpStage, wave, lane);
@@ -1366,11 +1449,13 @@ void tgemm_stream(SArgs a) {
       // end of step g: Q(g + 2) has landed and decoded W(g + 2) is written.
       // Stores issued right before this step are younger than Q(g + 2);
       // counting fewer operations than are younger is always safe.
-      if (after)
+      if (after == G::kStores)
         wait_barrier<G::kWaitEnd + G::kStores>();
+      else if (after == G::kStoresPair)
+        wait_barrier<G::kWaitEnd + G::kStoresPair>();
       else
         wait_barrier<G::kWaitEnd>();
-      after = false;
+      after = 0;
       gt = t1;
       gp ^= 1;
     }
@@ -1380,7 +1465,53 @@ void tgemm_stream(SArgs a) {
     const int32_t m0 = pos / a.tiles_c * BM, n0 = pos % a.tiles_c * BN;
     const int32_t rb = m0 + wave * TM + (lane & 15);
     const int32_t cb = n0 + (lane >> 4) * 4;
-    if (a.vec_out && m0 + BM <= a.R && n0 + BN <= a.Cc) {
+    // a one-step tile has not waited for anything issued after its row scales
+    if (scaled_out && a.nk < 2) wait_vm<0>();
+    const float *rsw = rs_s + TM * wave;
+    if (a.o.vec8 && m0 + BM <= a.R && n0 + BN <= a.Cc) {
+      // bf16: scale and convert in the MFMA layout (lane l: row l % 16, four
+      // columns -> two dwords), then give each lane 8 columns of a fragment
+      // pair's 32: lane L takes row L / 4, columns 8 (L % 4) .. + 7 (fragment
+      // jj for L % 4 < 2, jj + 1 otherwise), so four neighbouring lanes write
+      // one 64-byte run with 16-byte stores.  An odd last fragment moves four
+      // columns (8 bytes) to each lane, as the int32 path below does.
+      const int p4 = lane & 3;
+      const int sA = 4 * ((lane >> 2) + 32 * (p4 & 1)), sB = sA + 64;
+      const int src = 4 * ((lane >> 2) + 16 * p4);
+      const bool hi = p4 >= 2;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float r = rsw[(lane & 15) + 16 * i];
+        uint16_t *orow = static_cast<uint16_t *>(a.o.ptr) +
+                         (int64_t)(m0 + wave * TM + (lane >> 2) + 16 * i) * a.Cc + n0;
+        uint32_t d[FN][2];
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+          d[jj][0] = bf16_pack(scaled(acc[i][jj][0], r, a.o.cscal), scaled(acc[i][jj][1], r, a.o.cscal));
+          d[jj][1] = bf16_pack(scaled(acc[i][jj][2], r, a.o.cscal), scaled(acc[i][jj][3], r, a.o.cscal));
+        }
+#pragma unroll
+        for (int jj = 0; jj + 1 < FN; jj += 2) {
+          uint4 w;
+          const uint32_t a0 = __builtin_amdgcn_ds_bpermute(sA, d[jj][0]), a1 = __builtin_amdgcn_ds_bpermute(sA, d[jj][1]);
+          const uint32_t b0 = __builtin_amdgcn_ds_bpermute(sB, d[jj][0]), b1 = __builtin_amdgcn_ds_bpermute(sB, d[jj][1]);
+          const uint32_t c0 = __builtin_amdgcn_ds_bpermute(sA, d[jj + 1][0]), c1 = __builtin_amdgcn_ds_bpermute(sA, d[jj + 1][1]);
+          const uint32_t e0 = __builtin_amdgcn_ds_bpermute(sB, d[jj + 1][0]), e1 = __builtin_amdgcn_ds_bpermute(sB, d[jj + 1][1]);
+          w.x = hi ? c0 : a0;
+          w.y = hi ? c1 : a1;
+          w.z = hi ? e0 : b0;
+          w.w = hi ? e1 : b1;
+          *reinterpret_cast<uint4 *>(orow + 16 * jj + 8 * p4) = w;
+        }
+        if constexpr (FN % 2 == 1) {
+          uint2 w;
+          w.x = __builtin_amdgcn_ds_bpermute(src, d[FN - 1][0]);
+          w.y = __builtin_amdgcn_ds_bpermute(src, d[FN - 1][1]);
+          *reinterpret_cast<uint2 *>(orow + 16 * (FN - 1) + 4 * p4) = w;
+        }
+      }
+      after = G::kStoresPair;
+    } else if (a.o.vec && m0 + BM <= a.R && n0 + BN <= a.Cc) {
       // Lane l of a fragment holds row l % 16, so neighbouring lanes hit
       // different rows and a CU's stores drain at a third of the rate of
       // row-contiguous ones.  A lane permutation (ds_bpermute, no LDS memory)
@@ -1390,31 +1521,31 @@ void tgemm_stream(SArgs a) {
       const int32_t rp = m0 + wave * TM + (lane >> 2), cp = n0 + (lane & 3) * 4;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int32_t *orow = a.out + (int64_t)(rp + 16 * i) * a.Cc + cp;
+        const float r = scaled_out ? rsw[(lane >> 2) + 16 * i] : 0.f;
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
           v4i v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_ds_bpermute(src, acc[i][jj][e]);
-          *reinterpret_cast<v4i *>(orow + 16 * jj) = v;
+          put4(a.o, a.Cc, rp + 16 * i, cp + 16 * jj, v, r);
         }
       }
-      after = true;
+      after = G::kStores;
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int32_t row = rb + 16 * i;
         if (row >= a.R) continue;
-        int32_t *orow = a.out + (int64_t)row * a.Cc;
+        const float r = scaled_out ? rsw[(lane & 15) + 16 * i] : 0.f;
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
           const int32_t col = cb + 16 * jj;
-          if (a.vec_out && col + 3 < a.Cc) {
-            *reinterpret_cast<v4i *>(orow + col) = acc[i][jj];
+          if (a.o.vec && col + 3 < a.Cc) {
+            put4(a.o, a.Cc, row, col, acc[i][jj], r);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (col + e < a.Cc) orow[col + e] = acc[i][jj][e];
+              if (col + e < a.Cc) put1(a.o, a.Cc, row, col + e, acc[i][jj][e], r);
           }
         }
       }
@@ -1517,8 +1648,11 @@ hipError_t launch_op(const Args &a, int kernel, int tile, bool fast, hipStream_t
   }
 }
 
-int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t N, int64_t K,
-        hipStream_t stream) {
+// out: the output buffer, elements of `kind`; rs, cs, cscal: the scales of
+// the scaled kinds (rs per output row; cs per output column, or null and
+// cscal for every column)
+int run(int op, const int8_t *q, const void *p, void *out, int kind, const float *rs, const float *cs,
+        float cscal, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
@@ -1526,15 +1660,27 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   // operand byte sizes, for the overlap check
   const int64_t qbytes = op == DX ? M * N : M * K;
   const int64_t pbytes = op == DW ? M * N : N * (K / 4);
-  const int64_t obytes = s.R * s.Cc * 4;
+  const int64_t esz = kind == OUT_BF16 ? 2 : 4;
+  const int64_t obytes = s.R * s.Cc * esz;
   if (overlaps(out, obytes, q, qbytes) || overlaps(out, obytes, p, pbytes)) return TGEMM_ERR_ALIAS;
+  if (kind != OUT_I32 &&
+      (overlaps(out, obytes, rs, s.R * 4) || (cs && overlaps(out, obytes, cs, s.Cc * 4))))
+    return TGEMM_ERR_ALIAS;
+  Out o;
+  o.ptr = out;
+  o.rs = rs;
+  o.cs = cs;
+  o.cscal = cscal;
+  o.kind = kind;
+  o.vec = (s.Cc % 4 == 0 && aligned(out, 4 * esz)) ? 1 : 0;
+  o.vec8 = (kind == OUT_BF16 && s.Cc % 8 == 0 && aligned(out, 16)) ? 1 : 0;
 
   const int tile = pick_tile(s);
   const TileInfo &ti = kTileInfo[tile];
   Args a;
   a.q = q;
   a.p = p;
-  a.out = out;
+  a.o = o;
   a.R = s.R;
   a.Cc = s.Cc;
   a.L = s.L;
@@ -1543,7 +1689,6 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
   a.tiles_c = (int32_t)ceil_div(s.Cc, ti.bn);
   a.tiles = (int32_t)(ceil_div(s.R, ti.bm) * a.tiles_c);
   a.band_cols = pick_band_cols(op, M, N, K, a.tiles_c);
-  a.vec_out = (s.Cc % 4 == 0 && aligned(out, 16)) ? 1 : 0;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
   {
@@ -1552,7 +1697,7 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
       SArgs sa;
       sa.Q = q;
       sa.Wp = static_cast<const uint8_t *>(p);
-      sa.out = out;
+      sa.o = o;
       sa.R = (int32_t)s.R;
       sa.Cc = (int32_t)s.Cc;
       sa.L = (int32_t)s.L;
@@ -1561,7 +1706,6 @@ int run(int op, const int8_t *q, const void *p, int32_t *out, int64_t M, int64_t
       sa.tiles_c = sp.tiles_c;
       sa.tiles = sp.tiles;
       sa.nk = (int32_t)(s.L / BK);
-      sa.vec_out = a.vec_out;
       if (op == FWD)
         hipLaunchKernelGGL(tgemm_stream<FWD>, dim3(sp.grid), dim3(fs::kNT), 0, stream, sa);
       else
@@ -1588,19 +1732,43 @@ extern "C" {
 int ternary_gemm_s8(const int8_t *A, const uint8_t *Wpacked, int32_t *C, int64_t M, int64_t N,
                     int64_t K, hipStream_t stream) {
   if (!A || !Wpacked || !C) return TGEMM_ERR_NULL;
-  return run(FWD, A, Wpacked, C, M, N, K, stream);
+  return run(FWD, A, Wpacked, C, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream);
 }
 
 int ternary_gemm_s8_dx(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
   if (!dC || !Wpacked || !dX) return TGEMM_ERR_NULL;
-  return run(DX, dC, Wpacked, dX, M, N, K, stream);
+  return run(DX, dC, Wpacked, dX, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream);
 }
 
 int ternary_gemm_s8_dw(const int8_t *A, const int8_t *dC, int32_t *dW, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
   if (!A || !dC || !dW) return TGEMM_ERR_NULL;
-  return run(DW, A, dC, dW, M, N, K, stream);
+  return run(DW, A, dC, dW, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream);
+}
+
+int ternary_gemm_s8_scaled(const int8_t *A, const uint8_t *Wpacked, const float *a_row_scale,
+                           float w_scale, void *Y, int out_kind, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream) {
+  if (!A || !Wpacked || !a_row_scale || !Y) return TGEMM_ERR_NULL;
+  if (out_kind != TGEMM_OUT_F32 && out_kind != TGEMM_OUT_BF16) return TGEMM_ERR_KIND;
+  return run(FWD, A, Wpacked, Y, out_kind, a_row_scale, nullptr, w_scale, M, N, K, stream);
+}
+
+int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const float *dc_row_scale,
+                              float w_scale, void *dX, int out_kind, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream) {
+  if (!dC || !Wpacked || !dc_row_scale || !dX) return TGEMM_ERR_NULL;
+  if (out_kind != TGEMM_OUT_F32 && out_kind != TGEMM_OUT_BF16) return TGEMM_ERR_KIND;
+  return run(DX, dC, Wpacked, dX, out_kind, dc_row_scale, nullptr, w_scale, M, N, K, stream);
+}
+
+int ternary_gemm_s8_dw_scaled(const int8_t *A, const int8_t *dC, const float *a_col_scale,
+                              const float *dc_col_scale, void *dW, int out_kind, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream) {
+  if (!A || !dC || !a_col_scale || !dc_col_scale || !dW) return TGEMM_ERR_NULL;
+  if (out_kind != TGEMM_OUT_F32 && out_kind != TGEMM_OUT_BF16) return TGEMM_ERR_KIND;
+  return run(DW, A, dC, dW, out_kind, a_col_scale, dc_col_scale, 1.f, M, N, K, stream);
 }
 
 const char *ternary_gemm_status_str(int status) {
@@ -1612,6 +1780,7 @@ const char *ternary_gemm_status_str(int status) {
     case TGEMM_ERR_BOUND: return "the contraction is longer than the exact-int32 bound";
     case TGEMM_ERR_ALIAS: return "the output overlaps an input";
     case TGEMM_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case TGEMM_ERR_KIND: return "the output kind is not TGEMM_OUT_F32 or TGEMM_OUT_BF16";
     default: return "unknown status";
   }
 }
@@ -1638,7 +1807,7 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
       plan->band_cols = sp.tiles_c;
       plan->kernel = KSTREAM;
       plan->threads_per_workgroup = fs::kNT;
-      plan->lds_bytes = sp.lds;
+      plan->lds_bytes = sp.lds + fs::BM * 4;   // stages + the tile's row scales
       return TGEMM_OK;
     }
   }

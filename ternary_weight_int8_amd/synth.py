@@ -49,6 +49,8 @@ _M2 = np.uint64(0x94D049BB133111EB)
 STREAM_A = 0
 STREAM_CODES = 1
 STREAM_DC = 2
+STREAM_ROW_SCALE = 3
+STREAM_COL_SCALE = 4
 
 # elements generated per numpy pass; bounds the temporaries to a few hundred MB
 _CHUNK = 1 << 24
@@ -185,3 +187,15 @@ def extreme_inputs(seed: int, M: int, N: int, K: int):
     Wp[: N // 2] = 0x55
     Wp[N // 2:] = 0xAA
     return A, Wp
+
+
+def positive_scales(seed: int, stream: int, n: int, lo: float = 2.0 ** -10, hi: float = 2.0 ** -3) -> np.ndarray:
+    """float32 [n], log-uniform over [lo, hi): per-row or per-column scales for
+    the scaled outputs (the range of absmax / 127 of int8-quantized values)."""
+    u = splitmix64(seed, stream, n)
+    t = (u >> np.uint64(11)).astype(np.float64) / float(1 << 53)
+    return (lo * (hi / lo) ** t).astype(np.float32)
+
+
+# the weight scale of the scaled forward and dX calls in tests and benchmarks
+W_SCALE = 0.0371

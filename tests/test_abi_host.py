@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (B.OK, B.ERR_NULL, B.ERR_DIM, B.ERR_PACK, B.ERR_BOUND, B.ERR_ALIAS, B.ERR_HIP):
+    for st in (B.OK, B.ERR_NULL, B.ERR_DIM, B.ERR_PACK, B.ERR_BOUND, B.ERR_ALIAS, B.ERR_HIP, B.ERR_KIND):
         s = B.status_str(st)
         assert s and s != "unknown status"
     assert B.status_str(12345) == "unknown status"
@@ -228,3 +228,64 @@ def test_wrappers_refuse_host_tensors():
         B.ternary_gemm_s8(A, Wp)
     with pytest.raises(TypeError):
         B.ternary_gemm_s8(A.to(torch.int16), Wp)
+
+
+# ---------------------------------------------------------------------------
+# scaled entry points: argument checks (no GPU: every case below returns
+# before anything is launched)
+# ---------------------------------------------------------------------------
+
+SCALED = ("ternary_gemm_s8_scaled", "ternary_gemm_s8_dx_scaled", "ternary_gemm_s8_dw_scaled")
+
+
+def _scaled_args(name, base=0x100000):
+    # inputs, then scales, then the output, far apart; the second scale is a
+    # float for the forward and dX, a device address for dW
+    a, b, s0, out = base, base + (1 << 20), base + (2 << 20), base + (4 << 20)
+    s1 = base + (3 << 20) if name.endswith("dw_scaled") else 0.5
+    return [a, b, s0, s1, out]
+
+
+def test_scaled_status_string():
+    assert "TGEMM_OUT_F32" in B.status_str(B.ERR_KIND)
+
+
+@pytest.mark.parametrize("name", SCALED)
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4])
+def test_scaled_null_pointer_rejected(name, which):
+    args = _scaled_args(name)
+    if which == 3 and not name.endswith("dw_scaled"):
+        return  # the weight scale is a value, not a pointer
+    args[which] = None
+    assert B.call_raw_scaled(name, *args, B.OUT_BF16, 4, 4, 4) == B.ERR_NULL
+
+
+@pytest.mark.parametrize("name", SCALED)
+@pytest.mark.parametrize("kind", [0, 3, -1, 7])
+def test_scaled_kind_rejected(name, kind):
+    assert B.call_raw_scaled(name, *_scaled_args(name), kind, 4, 4, 4) == B.ERR_KIND
+
+
+@pytest.mark.parametrize("name", SCALED)
+def test_scaled_checks_as_plain(name):
+    # the plain calls' checks still apply: dimensions, packing, bounds
+    args = _scaled_args(name)
+    assert B.call_raw_scaled(name, *args, B.OUT_F32, 0, 4, 4) == B.ERR_DIM
+    if not name.endswith("dw_scaled"):
+        assert B.call_raw_scaled(name, *args, B.OUT_F32, 3, 5, 6) == B.ERR_PACK
+    else:
+        assert B.call_raw_scaled(name, *args, B.OUT_F32, 131072, 4, 4) == B.ERR_BOUND
+
+
+def test_scaled_output_overlapping_a_scale_rejected():
+    M, N, K = 8, 8, 16
+    a, b, s0, _, _ = _scaled_args("ternary_gemm_s8_scaled")
+    # bf16 output of 8 x 8 (128 bytes) ending inside the row scales
+    assert B.call_raw_scaled("ternary_gemm_s8_scaled", a, b, s0, 0.5, s0 - 64, B.OUT_BF16,
+                             M, N, K) == B.ERR_ALIAS
+    # dW: output over the column scales of dC
+    a, b, s0, s1, _ = _scaled_args("ternary_gemm_s8_dw_scaled")
+    assert B.call_raw_scaled("ternary_gemm_s8_dw_scaled", a, b, s0, s1, s1 + 4, B.OUT_F32,
+                             M, N, K) == B.ERR_ALIAS
+    # a bf16 output right after the row scales does not overlap them
+    assert B.plan("fwd", M, N, K).out_rows == M

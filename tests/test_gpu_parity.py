@@ -273,3 +273,98 @@ def test_shape_errors_raise():
     C = torch.zeros((4, 4), dtype=torch.int32, device=DEV)
     assert B.call_raw("ternary_gemm_s8", A6.data_ptr(), W1.data_ptr(), C.data_ptr(), 4, 4, 6) == B.ERR_PACK
     assert B.call_raw("ternary_gemm_s8", A6.data_ptr(), W1.data_ptr(), A6.data_ptr(), 4, 4, 4) == B.ERR_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# scaled outputs: the integer product times per-row and per-column scales,
+# stored as float32 or bfloat16; compared bit for bit with the oracle's
+# integer result scaled the same way (IEEE single precision, nearest-even
+# rounding, then nearest-even bfloat16)
+# ---------------------------------------------------------------------------
+
+SCALED_CASES = [
+    ("fwd", 16384, 3456, 1280),   # stream kernel, the timed shape (every element)
+    ("fwd", 16300, 3450, 640),    # stream kernel, ragged tiles, N % 4 != 0 (element stores)
+    ("fwd", 4096, 4608, 64),      # stream kernel, one step per tile
+    ("fwd", 15000, 3460, 192),    # stream kernel, N % 8 == 4: bf16 in 8-byte stores
+    ("fwd", 300, 272, 96),        # tiled kernel
+    ("fwd", 299, 271, 100),       # tiled kernel, guarded loads
+    ("dx", 16300, 3456, 1296),    # stream dX, ragged rows and columns
+    ("dx", 300, 96, 272),         # tiled dX
+    ("dw", 1090, 912, 4112),      # split dW kernel
+    ("dw", 97, 271, 299),         # tiled dW, ragged
+    ("dw", 16384, 3456, 1280),    # the timed shape
+]
+_int_results = {}
+
+
+def _scaled_case(op, M, N, K):
+    key = (op, M, N, K)
+    seed = M + 3 * N + 5 * K
+    if op == "fwd":
+        A, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+        ins = (A, Wp)
+        R, C = M, N
+    elif op == "dx":
+        dC, Wp = synth.dx_inputs(seed, M, N, K, 3)
+        ins = (dC, Wp)
+        R, C = M, K
+    else:
+        ins = synth.dw_inputs(seed, M, N, K)
+        R, C = K, N
+    rs = synth.positive_scales(seed, synth.STREAM_ROW_SCALE, R)
+    cs = (synth.positive_scales(seed, synth.STREAM_COL_SCALE, C) if op == "dw"
+          else np.float32(synth.W_SCALE))
+    if key not in _int_results:
+        _int_results.clear()
+        _int_results[key] = (oracle.fwd(*ins) if op == "fwd" else
+                             oracle.dx(ins[0], ins[1], K) if op == "dx" else oracle.dw(*ins))
+    return ins, rs, cs, _int_results[key]
+
+
+def _gpu_scaled(op, ins, K, rs, cs, dtype, out=None):
+    if op == "fwd":
+        return B.ternary_gemm_s8_scaled(dev(ins[0]), dev(ins[1]), dev(rs), float(cs), dtype, Y=out)
+    if op == "dx":
+        return B.ternary_gemm_s8_dx_scaled(dev(ins[0]), dev(ins[1]), K, dev(rs), float(cs), dtype, dX=out)
+    return B.ternary_gemm_s8_dw_scaled(dev(ins[0]), dev(ins[1]), dev(rs), dev(cs), dtype, dW=out)
+
+
+def _bits(t):
+    torch = _torch_mod()
+    return host(t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32))
+
+
+def _torch_mod():
+    import torch
+    return torch
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("op,M,N,K", SCALED_CASES)
+def test_scaled_outputs(op, M, N, K, kind):
+    torch = _torch_mod()
+    say(f"scaled {kind} {op} {M}x{N}x{K} plan={tile_of(op, M, N, K)}")
+    ins, rs, cs, acc = _scaled_case(op, M, N, K)
+    want = oracle.scale_output(acc, rs, cs, kind)
+    dtype = torch.float32 if kind == "f32" else torch.bfloat16
+    got = _bits(_gpu_scaled(op, ins, K, rs, cs, dtype))
+    want_bits = want.view(np.int32) if kind == "f32" else want.view(np.int16)
+    assert_exact(got, want_bits, f"scaled {kind} {op} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("op,M,N,K", [("fwd", 4096, 4608, 64), ("dx", 300, 96, 272), ("dw", 97, 271, 299)])
+def test_scaled_output_misaligned(op, M, N, K):
+    # a bf16 output starting 2 bytes into its buffer takes the element stores;
+    # the bytes around it stay untouched
+    torch = _torch_mod()
+    say(f"scaled bf16 misaligned {op} {M}x{N}x{K}")
+    ins, rs, cs, acc = _scaled_case(op, M, N, K)
+    R, C = acc.shape
+    buf = torch.full((R * C + 2,), -7, dtype=torch.int16, device=DEV)
+    out = buf[1:1 + R * C].view(torch.bfloat16).view(R, C)
+    _gpu_scaled(op, ins, K, rs, cs, torch.bfloat16, out=out)
+    b = host(buf)
+    assert b[0] == -7 and b[-1] == -7
+    assert_exact(b[1:1 + R * C].reshape(R, C), oracle.scale_output(acc, rs, cs, "bf16").view(np.int16),
+                 f"scaled misaligned {op}")

@@ -309,3 +309,68 @@ def test_negative_overflow_detected():
     dW, r = oracle.dw(A, dC, allow_overflow=True, return_overflows=True)
     assert r == 1
     assert int(dW[0, 0]) == -2147498880 + 2**32
+
+
+# ---------------------------------------------------------------------------
+# scaled outputs (the dequantization step after the integer product)
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_hand_values():
+    # catches: truncation instead of rounding, ties rounded up instead of to
+    # even, overflow not going to inf, sign or NaN handling
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -8 - 2 ** -20,
+                  -(1 + 3 * 2 ** -8), 3.3895313892515355e38, 3.4028234663852886e38, np.inf, -np.inf,
+                  0.0, -0.0, 2.0 ** -133, 2.0 ** -134, 2.0 ** -134 + 2.0 ** -140], dtype=np.float32)
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0x3F80, 0xBF82, 0x7F7F, 0x7F80, 0x7F80, 0xFF80,
+            0x0000, 0x8000, 0x0001, 0x0000, 0x0001]
+    assert [int(v) for v in oracle.bf16_nearest_even(x)] == want
+    nan = oracle.bf16_nearest_even(np.array([np.nan, -np.nan], dtype=np.float32))
+    assert all((int(v) & 0x7F80) == 0x7F80 and (int(v) & 0x7F) != 0 and (int(v) & 0x40) for v in nan)
+
+
+def test_bf16_rounding_matches_a_library():
+    # catches: any rounding mistake at all -- torch's float32 -> bfloat16 cast
+    # rounds to nearest even (NaN payloads excepted, checked above)
+    torch = pytest.importorskip("torch")
+    u = synth.splitmix64(11, 7, 1 << 20)
+    bits = (u >> np.uint64(32)).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_nearest_even(x), want)
+
+
+def test_scaled_f32_within_three_roundings_of_exact():
+    # catches: a dropped or swapped scale, a wrong row/column orientation, a
+    # product in lower precision -- the single-precision result must sit
+    # within three half-ulp roundings of the exact real product
+    R, C = 300, 272
+    acc = (synth.splitmix64(5, 9, R * C) >> np.uint64(33)).astype(np.int64)
+    acc = (acc - (1 << 30)).astype(np.int32).reshape(R, C)
+    rs = synth.positive_scales(5, synth.STREAM_ROW_SCALE, R)
+    cs = synth.positive_scales(5, synth.STREAM_COL_SCALE, C)
+    exact = acc.astype(np.float64) * rs.astype(np.float64)[:, None] * cs.astype(np.float64)[None, :]
+    y = oracle.scale_output(acc, rs, cs, "f32").astype(np.float64)
+    assert np.all(np.abs(y - exact) <= 3 * 2.0 ** -24 * np.abs(exact))
+    ys = oracle.scale_output(acc, rs, np.float32(synth.W_SCALE), "f32").astype(np.float64)
+    exact_s = acc.astype(np.float64) * rs.astype(np.float64)[:, None] * np.float64(np.float32(synth.W_SCALE))
+    assert np.all(np.abs(ys - exact_s) <= 3 * 2.0 ** -24 * np.abs(exact_s))
+    # bf16 is within half a bf16 ulp (2^-8 of the value at most) of the f32 result
+    yb = oracle.bf16_value(oracle.scale_output(acc, rs, cs, "bf16"))
+    assert np.all(np.abs(yb - y) <= 2.0 ** -8 * np.abs(y))
+
+
+def test_scaled_orientation_exact_case():
+    # catches: row scales applied to columns (or the reverse); with powers of
+    # two and small integers every value is exact
+    acc = np.array([[1, 2, 3], [4, 5, 6]], dtype=np.int32)
+    rs = np.array([0.5, 4.0], dtype=np.float32)
+    cs = np.array([1.0, 0.25, 8.0], dtype=np.float32)
+    want = np.array([[0.5, 0.25, 12.0], [16.0, 5.0, 192.0]], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.scale_output(acc, rs, cs, "f32"), want)
+    np.testing.assert_array_equal(oracle.scale_output(acc, rs, np.float32(2.0), "f32"),
+                                  acc * rs[:, None] * 2)
+    # int32 -> float32 rounds to nearest even above 2^24
+    big = np.array([[2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 31)]], dtype=np.int32)
+    got = oracle.scale_output(big, np.ones(1, np.float32), np.float32(1.0), "f32")
+    np.testing.assert_array_equal(got, np.array([[2.0 ** 24, 2.0 ** 24 + 4, -2.0 ** 31]], np.float32))
