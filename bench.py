@@ -103,6 +103,47 @@ def cpu_baseline(A, Wp, dC, K, rows):
     }
 
 
+def scaled_outputs(B, synth, torch, stream, Ad, Wd, dCd, M, N, K, seed, steps):
+    """Average launch time of each product with a scaled bf16 output (row and
+    column scales fused into the stores), on the step's inputs; not part of
+    the step's metric.  Bytes: inputs, scale vectors and the bf16 output."""
+    dev = Ad.device
+    rs_m = torch.from_numpy(synth.positive_scales(seed, synth.STREAM_ROW_SCALE, M)).to(dev)
+    rs_k = torch.from_numpy(synth.positive_scales(seed, synth.STREAM_ROW_SCALE, K)).to(dev)
+    cs_n = torch.from_numpy(synth.positive_scales(seed, synth.STREAM_COL_SCALE, N)).to(dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    runs = {
+        "fwd_bf16": (lambda: B.ternary_gemm_s8_scaled(Ad, Wd, rs_m, synth.W_SCALE, torch.bfloat16,
+                                                      Y=Y, stream=stream),
+                     M * K + N * (K // 4) + 4 * M + 2 * M * N),
+        "dx_bf16": (lambda: B.ternary_gemm_s8_dx_scaled(dCd, Wd, K, rs_m, synth.W_SCALE, torch.bfloat16,
+                                                        dX=dX, stream=stream),
+                    M * N + N * (K // 4) + 4 * M + 2 * M * K),
+        "dw_bf16": (lambda: B.ternary_gemm_s8_dw_scaled(Ad, dCd, rs_k, cs_n, torch.bfloat16, dW=dW,
+                                                        stream=stream),
+                    M * K + M * N + 4 * (K + N) + 2 * K * N),
+    }
+    out = {}
+    ops = 2 * M * N * K
+    for name, (fn, byts) in runs.items():
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[-1]) / steps / 1e3
+        out[name] = {"avg_us": t * 1e6, "tops": ops / t / 1e12, "mfma_frac": ops / t / PEAK_INT8_OPS,
+                     "gbps": byts / t / 1e9, "hbm_frac": byts / t / PEAK_HBM_BPS,
+                     "algorithmic_bytes": byts, "ops": ops}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +154,9 @@ def main():
                     help="rows of the batch the CPU oracle baseline runs on (0: skip)")
     ap.add_argument("--only", choices=["fwd", "dx", "dw"], default=None,
                     help="time a single product instead of the whole step (for profiling)")
+    ap.add_argument("--scaled-steps", type=int, default=20,
+                    help="after the timed step, time each product's scaled bf16 output "
+                         "(the dequantizing epilogue) over this many launches (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -238,6 +282,9 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.scaled_steps > 0 and not args.only:
+        line["scaled_outputs"] = scaled_outputs(B, synth, torch, stream, Ad, Wd, dCd, M, N, K,
+                                                args.seed, args.scaled_steps)
     if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:
         line["cpu_baseline"] = cpu_baseline(A, Wp, dC, K, min(args.cpu_rows, M))
     else:
