@@ -44,7 +44,7 @@ class TgemmPlan(ctypes.Structure):
     ]
 
 
-KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM = 0, 2, 3   # TgemmPlan.kernel
+KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM, KERNEL_SKINNY = 0, 2, 3, 4   # TgemmPlan.kernel
 
 
 class TernaryGemmError(RuntimeError):

@@ -1559,6 +1559,175 @@ void tgemm_stream(SArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Skinny forward kernel (tgemm_skinny): C[M][N] with at most 32 rows.  Here
+// the packed weights are nearly all of the bytes moved, so the product is
+// bound by reading them from HBM, and keeping W as 2-bit codes reads a
+// quarter of the bytes of int8 weights [P10425 "How each column was
+// measured"].
+//
+// A workgroup of 8 waves owns BN = 16 NB output columns and all the rows.
+// Its waves split the contraction into super-steps of 256 (wave w takes
+// super-steps w, w + 8, ...); the eight partial sums are added at the end in
+// LDS, in wave order.  The main loop touches no LDS: per super-step each lane
+// loads, a super-step ahead, straight into registers
+//   W: 16 bytes (64 codes) of packed row n0 + 16 nb + lane % 16, per block nb,
+//   A: 64 bytes of row 16 mf + lane % 16, per 16-row block mf,
+// both at contraction 256 s + 64 g (g = lane / 16), and decodes the weights
+// there (decode16).  Sub-step q of the super-step pairs packed dword q with A
+// bytes 16 q .. 16 q + 15: the same 16 contraction indices, so each of the
+// four MFMA sub-steps covers 64 distinct indices and together they cover the
+// super-step.  A contraction that ends inside a super-step (K % 256 != 0,
+// K % 64 == 0) is finished by one more step whose lanes past the end load an
+// in-range group and zero its codes (code 0 is weight 0).  Rows and columns
+// past the output load the last valid row (computed, never stored).
+// ---------------------------------------------------------------------------
+namespace sk {
+constexpr int kWaves = 8, kNT = 64 * kWaves;
+constexpr int SK = 256;   // contraction per super-step: four MFMA steps of 64
+}  // namespace sk
+
+struct KArgs {
+  const int8_t *A;
+  const uint8_t *Wp;
+  Out o;              // column scale, when scaled: o.cscal (o.cs is null)
+  int32_t M, N, K;
+  int32_t nfull;      // whole super-steps, K / 256
+  int32_t vq;         // 64-steps of the last, partial super-step (K % 256 / 64), or 0
+};
+
+// Reduction buffer: per wave, the tile's 16 MF rows of 4 NB column quads
+// (v4i), each row padded by one quad so that the MFMA-layout writes (lanes on
+// 16 rows) hit 16 distinct bank groups.
+template <int MF, int NB>
+struct SkLds {
+  static constexpr int kPitch = 4 * NB + 1;
+  static constexpr int kWave = 16 * MF * kPitch;
+  static constexpr int kBytes = sk::kWaves * kWave * 16;
+  static_assert(kBytes <= 80 * 1024, "two workgroups per CU");
+};
+
+template <int MF, int NB>
+__device__ __forceinline__ void sk_load(v4i (&w)[NB], v4i (&x)[MF][4], const uint8_t *const (&wr)[NB],
+                                        const int8_t *const (&ar)[MF], int64_t wo, int64_t ao) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) w[nb] = *reinterpret_cast<const v4i *>(wr[nb] + wo);
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[mf][q] = *reinterpret_cast<const v4i *>(ar[mf] + ao + 16 * q);
+}
+
+template <int MF, int NB>
+__device__ __forceinline__ void sk_step(v4i (&acc)[MF][NB], const v4i (&w)[NB], const v4i (&x)[MF][4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const v4i d = decode16((uint32_t)w[nb][q]);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+        acc[mf][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(d, x[mf][q], acc[mf][nb], 0, 0, 0);
+    }
+}
+
+template <int MF, int NB>
+__global__ __attribute__((amdgpu_flat_work_group_size(sk::kNT, sk::kNT), amdgpu_waves_per_eu(2)))
+void tgemm_skinny(KArgs a) {
+  typedef SkLds<MF, NB> L;
+  __shared__ v4i red[sk::kWaves * L::kWave];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int32_t n0 = (int32_t)blockIdx.x * 16 * NB;
+  const int64_t kb = a.K / 4;
+
+  const uint8_t *wr[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int32_t n = n0 + 16 * nb + r;
+    wr[nb] = a.Wp + (int64_t)(n < a.N ? n : a.N - 1) * kb + 16 * g;
+  }
+  const int8_t *ar[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int32_t m = 16 * mf + r;
+    ar[mf] = a.A + (int64_t)(m < a.M ? m : a.M - 1) * a.K + 64 * g;
+  }
+  v4i acc[MF][NB];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mf][nb] = v4i{0, 0, 0, 0};
+
+  // whole super-steps: the wave's are wave + 8 i, i < cnt.  Two per
+  // iteration through two register sets; each load is issued a super-step
+  // before its use (past the wave's last super-step the load repeats it: in
+  // range, never used).
+  const int32_t cnt = a.nfull > wave ? (a.nfull - wave + sk::kWaves - 1) / sk::kWaves : 0;
+  if (cnt > 0) {
+    v4i w0[NB], x0[MF][4], w1[NB], x1[MF][4];
+    const int32_t last = wave + sk::kWaves * (cnt - 1);
+    sk_load<MF, NB>(w0, x0, wr, ar, 64 * (int64_t)wave, sk::SK * (int64_t)wave);
+    int32_t s = wave;
+    for (int32_t i = 0; i + 2 <= cnt; i += 2) {
+      const int32_t s1 = s + sk::kWaves;
+      const int32_t s2 = s1 + sk::kWaves < last ? s1 + sk::kWaves : last;
+      sk_load<MF, NB>(w1, x1, wr, ar, 64 * (int64_t)s1, sk::SK * (int64_t)s1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      sk_step<MF, NB>(acc, w0, x0);
+      sk_load<MF, NB>(w0, x0, wr, ar, 64 * (int64_t)s2, sk::SK * (int64_t)s2);
+      __builtin_amdgcn_sched_barrier(0);
+      sk_step<MF, NB>(acc, w1, x1);
+      s += 2 * sk::kWaves;
+    }
+    if (cnt & 1) sk_step<MF, NB>(acc, w0, x0);   // super-step `last`
+  }
+  // the partial super-step, on the wave whose turn it is
+  if (a.vq && wave == a.nfull % sk::kWaves) {
+    const int32_t s = a.nfull;
+    const int gd = (g < a.vq ? g : a.vq - 1) - g;   // lanes past the end: the last group in range
+    v4i w[NB], x[MF][4];
+    sk_load<MF, NB>(w, x, wr, ar, 64 * (int64_t)s + 16 * gd, sk::SK * (int64_t)s + 64 * gd);
+    if (g >= a.vq) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) w[nb] = v4i{0, 0, 0, 0};
+    }
+    sk_step<MF, NB>(acc, w, x);
+  }
+
+  // partial sums -> LDS (row 16 mf + lane % 16, quad 4 nb + lane / 16 of the tile)
+  v4i *mine = red + wave * L::kWave;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mine[(16 * mf + r) * L::kPitch + 4 * nb + g] = acc[mf][nb];
+  __syncthreads();
+
+  // thread t sums quad t % (4 NB) of tile row t / (4 NB) over the waves, in
+  // wave order, and stores it: neighbouring threads write neighbouring
+  // 16-byte pieces of one output row
+  constexpr int kQuads = 4 * NB, kOut = 16 * MF * kQuads;
+  static_assert(kOut <= sk::kNT, "one quad per thread");
+  if (tid < kOut) {
+    const int m = tid / kQuads, cq = tid % kQuads;
+    v4i s = red[m * L::kPitch + cq];
+#pragma unroll
+    for (int w = 1; w < sk::kWaves; ++w) s += red[w * L::kWave + m * L::kPitch + cq];
+    const int32_t col = n0 + 4 * cq;
+    if (m < a.M) {
+      const float rsc = row_scale(a.o, m);
+      if (a.o.vec && col + 3 < a.N) {
+        put4(a.o, a.N, m, col, s, rsc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < a.N) put1(a.o, a.N, m, col + e, s[e], rsc);
+      }
+    }
+  }
+}
+
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -1574,10 +1743,12 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 // Kernel per product, tile and load path:
 //   tiled  tgemm_kernel: every case but the next
 //   split  tgemm_dw_split: dW, 128 x 144 tile, contraction of 8 steps or more
+//   stream tgemm_stream: large forward and dX outputs (stream_plan)
+//   skinny tgemm_skinny: forward with at most 32 rows (skinny_plan)
 // (A variant that loads the int8 operand of the forward and dX straight into
 // MFMA registers, without LDS, measured no faster in the three-product step
 // on MI355X and was left out.)
-enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3 };
+enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3, KSKINNY = 4 };
 
 // The streaming kernels (forward, dX): apply when the contraction is a whole
 // number of steps, the operands are aligned for their 16- and 4-byte loads
@@ -1606,6 +1777,33 @@ StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
   sp.tiles = (int32_t)(tr * tc);
   sp.grid = kStreamCUs;
   return sp;
+}
+
+// The skinny forward: at most 32 rows, K % 64 == 0 (whole 64-steps, packed
+// rows in whole 16-byte pieces), 16-byte aligned A and Wpacked.  Column
+// blocks of 64, 32 or 16: the widest that still gives 128 workgroups or more
+// (A is re-read by every workgroup, so wider blocks read fewer bytes).
+struct SkinnyPlan {
+  bool ok;
+  int32_t mf, nb, grid, lds;
+};
+
+SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+  SkinnyPlan kp{};
+  if (op != FWD || M > 32 || K % 64 != 0 || qalign % 16 != 0 || walign % 16 != 0) return kp;
+  if (N > INT32_MAX - 64 || K > INT32_MAX) return kp;
+  kp.mf = M > 16 ? 2 : 1;
+  kp.nb = N >= 128 * 64 ? 4 : N >= 128 * 32 ? 2 : 1;
+  kp.grid = (int32_t)ceil_div(N, 16 * kp.nb);
+  kp.lds = sk::kWaves * 16 * kp.mf * (4 * kp.nb + 1) * 16;
+  kp.ok = true;
+  return kp;
+}
+
+template <int MF, int NB>
+void launch_skinny(const KArgs &ka, int grid, hipStream_t stream) {
+  static_assert(SkLds<MF, NB>::kBytes == sk::kWaves * 16 * MF * (4 * NB + 1) * 16, "plan LDS");
+  hipLaunchKernelGGL((tgemm_skinny<MF, NB>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
 }
 
 int pick_kernel(int op, int tile, int64_t L) {
@@ -1691,6 +1889,30 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   a.band_cols = pick_band_cols(op, M, N, K, a.tiles_c);
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
+  {
+    const SkinnyPlan kp = skinny_plan(op, M, N, K, align_of(q), align_of(p));
+    if (kp.ok) {
+      KArgs ka;
+      ka.A = q;
+      ka.Wp = static_cast<const uint8_t *>(p);
+      ka.o = o;
+      ka.M = (int32_t)M;
+      ka.N = (int32_t)N;
+      ka.K = (int32_t)K;
+      ka.nfull = (int32_t)(K / sk::SK);
+      ka.vq = (int32_t)(K % sk::SK / BK);
+      const int sel = 10 * kp.mf + kp.nb;
+      switch (sel) {
+        case 11: launch_skinny<1, 1>(ka, kp.grid, stream); break;
+        case 12: launch_skinny<1, 2>(ka, kp.grid, stream); break;
+        case 14: launch_skinny<1, 4>(ka, kp.grid, stream); break;
+        case 21: launch_skinny<2, 1>(ka, kp.grid, stream); break;
+        case 22: launch_skinny<2, 2>(ka, kp.grid, stream); break;
+        default: launch_skinny<2, 4>(ka, kp.grid, stream); break;
+      }
+      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+    }
+  }
   {
     const StreamPlan sp = stream_plan(op, M, N, K, align_of(q), align_of(p));
     if (sp.ok) {
@@ -1797,6 +2019,21 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->contraction = s.L;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   {
+    const SkinnyPlan kp = skinny_plan(op, M, N, K, al, al);
+    if (kp.ok) {
+      plan->tile_rows = 16 * kp.mf;
+      plan->tile_cols = 16 * kp.nb;
+      plan->tiles = kp.grid;
+      plan->workgroups = kp.grid;
+      plan->tiles_per_workgroup = 1;
+      plan->band_cols = kp.grid;
+      plan->kernel = KSKINNY;
+      plan->threads_per_workgroup = sk::kNT;
+      plan->lds_bytes = kp.lds;
+      return TGEMM_OK;
+    }
+  }
+  {
     const StreamPlan sp = stream_plan(op, M, N, K, al, al);
     if (sp.ok) {
       plan->tile_rows = fs::BM;
@@ -1849,6 +2086,11 @@ int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iter
     if (pos >= cnt) return TGEMM_ERR_DIM;
     tr = (int32_t)((start + pos) / tiles_c);
     tc = (int32_t)((start + pos) % tiles_c);
+  } else if (plan->kernel == KSKINNY) {
+    // workgroup b: column block b, all rows
+    if (iteration != 0) return TGEMM_ERR_DIM;
+    tr = 0;
+    tc = (int32_t)workgroup;
   } else {
     if (iteration != 0) return TGEMM_ERR_DIM;
     tile_rc(xcd_tile((int32_t)workgroup, tiles), tiles / tiles_c, tiles_c, plan->band_cols, &tr, &tc);

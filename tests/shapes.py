@@ -37,3 +37,12 @@ STREAM_SHAPES = [(16300, 3450, 640), (15000, 3460, 192), (4096, 4608, 64), (8192
 # least 256 tiles of 512 x 160): the timed shape, ragged M with a last column
 # tile of 16 or 144 of its 160 columns, and one or two contraction steps.
 DX_STREAM_SHAPES = [(16300, 3456, 1296), (15000, 2048, 1424), (8192, 64, 5120), (4096, 128, 10240)]
+
+# Shapes for the skinny forward kernel (M <= 32, K % 64 == 0): one and two
+# 16-row blocks, column blocks of 16, 32 and 64 with ragged last blocks (N % 4
+# != 0 has no 16-byte stores), contractions that end inside a super-step of
+# 256 (one, two or three 64-steps left) or in a whole one, fewer super-steps
+# than waves, and the pages' row count at their weight shapes.
+SKINNY_SHAPES = [(1, 16, 64), (16, 100, 192), (17, 3456, 1280), (27, 3456, 1280), (27, 1280, 3456),
+                 (32, 4099, 2112), (5, 8200, 4160), (1, 16384, 16384), (27, 16384, 16384),
+                 (32, 65, 64), (2, 4096, 512), (31, 8256, 768)]

@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, STREAM_SHAPES, TILES
+from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_SHAPES, STREAM_SHAPES, TILES
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -118,7 +118,8 @@ def _coverage(op, M, N, K):
     ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
-    + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES])
+    + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES]
+    + [("fwd",) + s for s in SKINNY_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.lds_bytes <= 160 * 1024
@@ -126,6 +127,9 @@ def test_every_output_tile_covered_once(op, M, N, K):
         assert pl.threads_per_workgroup == 512 and pl.workgroups == 256
         per_xcd = -(-pl.tiles // 8)
         assert pl.tiles_per_workgroup == -(-per_xcd // 32)
+    elif pl.kernel == B.KERNEL_SKINNY:
+        assert pl.threads_per_workgroup == 512 and pl.tile_rows in (16, 32) and pl.tile_rows >= M
+        assert pl.workgroups == pl.tiles and pl.tiles_per_workgroup == 1
     else:
         assert pl.threads_per_workgroup == (512 if pl.kernel == B.KERNEL_SPLIT else 256)
         assert pl.workgroups == pl.tiles and pl.tiles_per_workgroup == 1
@@ -134,11 +138,12 @@ def test_every_output_tile_covered_once(op, M, N, K):
 def test_parity_shapes_reach_every_tile_and_path():
     # the GPU parity shape lists exercise every tile shape on both load paths,
     # and every kernel on each load path it serves
-    kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
+    kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1),
+                       (B.KERNEL_SKINNY, 1)},
                "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES), ("dx", DX_SHAPES + DX_STREAM_SHAPES),
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES), ("dx", DX_SHAPES + DX_STREAM_SHAPES),
                        ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
         for s in shapes:
@@ -167,6 +172,25 @@ def test_kernel_choice():
     assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
     for s in STREAM_SHAPES:
         assert B.plan("fwd", *s).kernel == B.KERNEL_STREAM, s
+    for s in SKINNY_SHAPES:
+        assert B.plan("fwd", *s).kernel == B.KERNEL_SKINNY, s
+    assert B.plan("fwd", 33, 16384, 16384).kernel != B.KERNEL_SKINNY   # more than 32 rows
+    assert B.plan("fwd", 27, 16384, 16352).kernel == B.KERNEL_TILED    # K % 64 != 0
+    assert B.plan("fwd", 27, 16384, 16384, align=8).kernel == B.KERNEL_TILED
+    assert B.plan("dx", 27, 16384, 16384).kernel == B.KERNEL_TILED     # forward only
+
+
+def test_skinny_plan():
+    # column blocks of 64, 32, 16: the widest that leaves 128 workgroups or more
+    for (M, N, K), (rows, cols) in {(27, 16384, 16384): (32, 64), (16, 8192, 1280): (16, 64),
+                                    (27, 8191, 1280): (32, 32), (1, 4096, 256): (16, 32),
+                                    (32, 4095, 64): (32, 16), (17, 3456, 1280): (32, 16)}.items():
+        pl = B.plan("fwd", M, N, K)
+        assert pl.kernel == B.KERNEL_SKINNY and (pl.tile_rows, pl.tile_cols) == (rows, cols), (M, N, K)
+        assert pl.tiles == pl.workgroups == -(-N // cols)
+        # 8 waves' partial sums of the tile, rows padded by one 16-byte quad
+        assert pl.lds_bytes == 8 * rows * (cols // 4 + 1) * 16
+        assert B.tile_of(pl, 3) == (0, 3 * cols)
 
 
 def test_tile_query_out_of_range():

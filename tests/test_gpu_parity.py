@@ -14,7 +14,7 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
-from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, STREAM_SHAPES
+from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_SHAPES, STREAM_SHAPES
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -167,6 +167,28 @@ def test_fwd_stream_shapes(M, N, K):
     assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd stream {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_fwd_skinny_shapes(M, N, K):
+    say(f"fwd skinny {M}x{N}x{K} plan={tile_of('fwd', M, N, K)}")
+    assert B.plan("fwd", M, N, K).kernel == B.KERNEL_SKINNY
+    A, Wp = synth.fwd_inputs(M * 13 + N + K, M, N, K, 4)
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd skinny {M}x{N}x{K}")
+
+
+def test_skinny_extreme():
+    # the int32 extremes through the skinny kernel: A row 0 all -128, row 1
+    # uniform; codes +1 in columns < 16, -1 in the rest; K = 16777152, the
+    # longest whole number of 64-steps inside the exact-int32 bound
+    M, N, K = 2, 32, 16777152
+    say(f"fwd skinny extreme {M}x{N}x{K}")
+    assert B.plan("fwd", M, N, K).kernel == B.KERNEL_SKINNY
+    A, Wp = synth.extreme_inputs(1, M, N, K)
+    C = gpu_fwd(A, Wp)
+    assert (C[0, :16] == -128 * K).all() and (C[0, 16:] == 128 * K).all()
+    assert -128 * K == -2147475456
+    assert_exact(C, oracle.fwd(A, Wp), "skinny extreme vs oracle")
+
+
 @pytest.mark.parametrize("M,N,K", DX_STREAM_SHAPES)
 def test_dx_stream_shapes(M, N, K):
     say(f"dx stream {M}x{N}x{K} plan={tile_of('dx', M, N, K)}")
@@ -217,7 +239,8 @@ def test_misaligned_bases(offset):
 
 
 @pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 1900, 80),
-                                      ("dx", 299, 100, 268), ("dw", 97, 271, 299)])
+                                      ("fwd", 27, 4099, 2112), ("dx", 299, 100, 268),
+                                      ("dw", 97, 271, 299)])
 def test_writes_exactly_the_output(op, M, N, K):
     # the output sits between two canary bands inside one buffer, pre-filled
     # with a sentinel no result here can take; afterwards every output element
@@ -289,6 +312,9 @@ SCALED_CASES = [
     ("fwd", 15000, 3460, 192),    # stream kernel, N % 8 == 4: bf16 in 8-byte stores
     ("fwd", 300, 272, 96),        # tiled kernel
     ("fwd", 299, 271, 100),       # tiled kernel, guarded loads
+    ("fwd", 27, 16384, 16384),    # skinny kernel, the skinny workload
+    ("fwd", 32, 4099, 2112),      # skinny kernel, ragged columns (element stores)
+    ("fwd", 5, 8200, 4160),       # skinny kernel, one 16-row block
     ("dx", 16300, 3456, 1296),    # stream dX, ragged rows and columns
     ("dx", 300, 96, 272),         # tiled dX
     ("dw", 1090, 912, 4112),      # split dW kernel
