@@ -1569,18 +1569,25 @@ void tgemm_stream(SArgs a) {
 // A workgroup of 8 waves owns BN = 16 NB output columns and all the rows.
 // Its waves split the contraction into super-steps of 256 (wave w takes
 // super-steps w, w + 8, ...); the eight partial sums are added at the end in
-// LDS, in wave order.  The main loop touches no LDS: per super-step each lane
-// loads, a super-step ahead, straight into registers
+// LDS, in wave order.  Per super-step each lane loads, a super-step ahead,
+// straight into registers
 //   W: 16 bytes (64 codes) of packed row n0 + 16 nb + lane % 16, per block nb,
-//   A: 64 bytes of row 16 mf + lane % 16, per 16-row block mf,
-// both at contraction 256 s + 64 g (g = lane / 16), and decodes the weights
-// there (decode16).  Sub-step q of the super-step pairs packed dword q with A
-// bytes 16 q .. 16 q + 15: the same 16 contraction indices, so each of the
-// four MFMA sub-steps covers 64 distinct indices and together they cover the
-// super-step.  A contraction that ends inside a super-step (K % 256 != 0,
-// K % 64 == 0) is finished by one more step whose lanes past the end load an
-// in-range group and zero its codes (code 0 is weight 0).  Rows and columns
-// past the output load the last valid row (computed, never stored).
+//      at contraction 256 s + 64 g (g = lane / 16),
+//   A: the super-step's 256 bytes of each of the 16 MF rows, either
+//      (AL false) as 64 bytes of row 16 mf + lane % 16 at 64 g, or
+//      (AL true, more than 8 rows) in whole 128-byte lines, instruction i of
+//      block mf taking row 16 mf + 4 i + g, 16-byte chunk lane % 16; the lines
+//      go through a wave-private LDS tile into the MFMA layout (partial-line
+//      requests, 16 rows x 4 pieces per instruction, held the L1 to a third
+//      of its whole-line rate),
+// and decodes the weights in registers (decode16).  Sub-step q pairs packed
+// dword q with A chunk 4 g + q of the super-step: the same 16 contraction
+// indices, so each of the four MFMA sub-steps covers 64 distinct indices and
+// together they cover the super-step.  A contraction that ends inside a
+// super-step (K % 256 != 0, K % 64 == 0) is finished by one more step whose
+// lanes past the end load in-range bytes and zero their codes (code 0 is
+// weight 0).  Rows and columns past the output load the last valid row
+// (computed, never stored).
 // ---------------------------------------------------------------------------
 namespace sk {
 constexpr int kWaves = 8, kNT = 64 * kWaves;
@@ -1596,46 +1603,74 @@ struct KArgs {
   int32_t vq;         // 64-steps of the last, partial super-step (K % 256 / 64), or 0
 };
 
-// Reduction buffer: per wave, the tile's 16 MF rows of 4 NB column quads
-// (v4i), each row padded by one quad so that the MFMA-layout writes (lanes on
-// 16 rows) hit 16 distinct bank groups.
-template <int MF, int NB>
+// LDS: the reduction buffer (per wave, the tile's 16 MF rows of 4 NB column
+// quads, each row padded by one quad so that the MFMA-layout writes, lanes on
+// 16 rows, hit 16 distinct bank groups); with AL, first the waves' A tiles
+// (16 MF rows of 256 bytes, chunk c of row m at slot c ^ (m & 15), so that
+// both the line writes and the fragment reads are conflict-free), in the same
+// memory.
+template <int MF, int NB, bool AL>
 struct SkLds {
   static constexpr int kPitch = 4 * NB + 1;
   static constexpr int kWave = 16 * MF * kPitch;
-  static constexpr int kBytes = sk::kWaves * kWave * 16;
+  static constexpr int kRed = sk::kWaves * kWave * 16;
+  static constexpr int kATile = 16 * MF * 256;
+  static constexpr int kTiles = AL ? sk::kWaves * kATile : 0;
+  static constexpr int kBytes = kRed > kTiles ? kRed : kTiles;
   static_assert(kBytes <= 80 * 1024, "two workgroups per CU");
 };
 
-template <int MF, int NB>
+template <int MF, bool AL>
+struct SkA {
+  typedef const int8_t *Ptr[MF][AL ? 4 : 1];
+};
+
+template <int MF, int NB, bool AL>
 __device__ __forceinline__ void sk_load(v4i (&w)[NB], v4i (&x)[MF][4], const uint8_t *const (&wr)[NB],
-                                        const int8_t *const (&ar)[MF], int64_t wo, int64_t ao) {
+                                        const typename SkA<MF, AL>::Ptr &ar, int64_t wo, int64_t ao) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) w[nb] = *reinterpret_cast<const v4i *>(wr[nb] + wo);
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) x[mf][q] = *reinterpret_cast<const v4i *>(ar[mf] + ao + 16 * q);
+    for (int i = 0; i < 4; ++i)
+      x[mf][i] = *reinterpret_cast<const v4i *>(AL ? ar[mf][AL ? i : 0] + ao : ar[mf][0] + ao + 16 * i);
 }
 
-template <int MF, int NB>
-__device__ __forceinline__ void sk_step(v4i (&acc)[MF][NB], const v4i (&w)[NB], const v4i (&x)[MF][4]) {
+template <int MF, int NB, bool AL>
+__device__ __forceinline__ void sk_step(v4i (&acc)[MF][NB], const v4i (&w)[NB], const v4i (&x)[MF][4],
+                                        int8_t *tile, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  if constexpr (AL) {
+    // lines -> tile: row 16 mf + 4 i + g, chunk r
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<v4i *>(tile + (16 * mf + 4 * i + g) * 256 + 16 * (r ^ (4 * i + g))) = x[mf][i];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v4i xa[MF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+      xa[mf] = AL ? *reinterpret_cast<const v4i *>(tile + (16 * mf + r) * 256 + 16 * ((4 * g + q) ^ r))
+                  : x[mf][q];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const v4i d = decode16((uint32_t)w[nb][q]);
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf)
-        acc[mf][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(d, x[mf][q], acc[mf][nb], 0, 0, 0);
+        acc[mf][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(d, xa[mf], acc[mf][nb], 0, 0, 0);
     }
+  }
 }
 
-template <int MF, int NB>
+template <int MF, int NB, bool AL>
 __global__ __attribute__((amdgpu_flat_work_group_size(sk::kNT, sk::kNT), amdgpu_waves_per_eu(2)))
 void tgemm_skinny(KArgs a) {
-  typedef SkLds<MF, NB> L;
-  __shared__ v4i red[sk::kWaves * L::kWave];
+  typedef SkLds<MF, NB, AL> L;
+  __shared__ __attribute__((aligned(256))) int8_t smem[L::kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -1648,12 +1683,15 @@ void tgemm_skinny(KArgs a) {
     const int32_t n = n0 + 16 * nb + r;
     wr[nb] = a.Wp + (int64_t)(n < a.N ? n : a.N - 1) * kb + 16 * g;
   }
-  const int8_t *ar[MF];
+  typename SkA<MF, AL>::Ptr ar;
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    const int32_t m = 16 * mf + r;
-    ar[mf] = a.A + (int64_t)(m < a.M ? m : a.M - 1) * a.K + 64 * g;
-  }
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int i = 0; i < (AL ? 4 : 1); ++i) {
+      const int32_t m = AL ? 16 * mf + 4 * i + g : 16 * mf + r;
+      ar[mf][i] = a.A + (int64_t)(m < a.M ? m : a.M - 1) * a.K + (AL ? 16 * r : 64 * g);
+    }
+  int8_t *tile = smem + (AL ? wave * L::kATile : 0);
   v4i acc[MF][NB];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
@@ -1668,35 +1706,41 @@ void tgemm_skinny(KArgs a) {
   if (cnt > 0) {
     v4i w0[NB], x0[MF][4], w1[NB], x1[MF][4];
     const int32_t last = wave + sk::kWaves * (cnt - 1);
-    sk_load<MF, NB>(w0, x0, wr, ar, 64 * (int64_t)wave, sk::SK * (int64_t)wave);
+    sk_load<MF, NB, AL>(w0, x0, wr, ar, 64 * (int64_t)wave, sk::SK * (int64_t)wave);
     int32_t s = wave;
     for (int32_t i = 0; i + 2 <= cnt; i += 2) {
       const int32_t s1 = s + sk::kWaves;
       const int32_t s2 = s1 + sk::kWaves < last ? s1 + sk::kWaves : last;
-      sk_load<MF, NB>(w1, x1, wr, ar, 64 * (int64_t)s1, sk::SK * (int64_t)s1);
+      sk_load<MF, NB, AL>(w1, x1, wr, ar, 64 * (int64_t)s1, sk::SK * (int64_t)s1);
       __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
-      sk_step<MF, NB>(acc, w0, x0);
-      sk_load<MF, NB>(w0, x0, wr, ar, 64 * (int64_t)s2, sk::SK * (int64_t)s2);
+      sk_step<MF, NB, AL>(acc, w0, x0, tile, lane);
+      sk_load<MF, NB, AL>(w0, x0, wr, ar, 64 * (int64_t)s2, sk::SK * (int64_t)s2);
       __builtin_amdgcn_sched_barrier(0);
-      sk_step<MF, NB>(acc, w1, x1);
+      sk_step<MF, NB, AL>(acc, w1, x1, tile, lane);
       s += 2 * sk::kWaves;
     }
-    if (cnt & 1) sk_step<MF, NB>(acc, w0, x0);   // super-step `last`
+    if (cnt & 1) sk_step<MF, NB, AL>(acc, w0, x0, tile, lane);   // super-step `last`
   }
-  // the partial super-step, on the wave whose turn it is
+  // the partial super-step, on the wave whose turn it is: weights of lanes
+  // with g >= vq (codes past K) are zeroed, and every lane loads in range:
+  // W at the last group in range, A at the last chunk in range
   if (a.vq && wave == a.nfull % sk::kWaves) {
     const int32_t s = a.nfull;
-    const int gd = (g < a.vq ? g : a.vq - 1) - g;   // lanes past the end: the last group in range
+    const int gd = (g < a.vq ? g : a.vq - 1) - g;
+    const int ad = AL ? (r < 4 * a.vq ? r : 4 * a.vq - 1) - r : 4 * gd;
     v4i w[NB], x[MF][4];
-    sk_load<MF, NB>(w, x, wr, ar, 64 * (int64_t)s + 16 * gd, sk::SK * (int64_t)s + 64 * gd);
+    sk_load<MF, NB, AL>(w, x, wr, ar, 64 * (int64_t)s + 16 * gd, sk::SK * (int64_t)s + 16 * ad);
     if (g >= a.vq) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) w[nb] = v4i{0, 0, 0, 0};
     }
-    sk_step<MF, NB>(acc, w, x);
+    sk_step<MF, NB, AL>(acc, w, x, tile, lane);
   }
 
-  // partial sums -> LDS (row 16 mf + lane % 16, quad 4 nb + lane / 16 of the tile)
+  // partial sums -> LDS (row 16 mf + lane % 16, quad 4 nb + lane / 16 of the
+  // tile); with AL the buffer reuses the A tiles, once every wave is done
+  if constexpr (AL) __syncthreads();
+  v4i *red = reinterpret_cast<v4i *>(smem);
   v4i *mine = red + wave * L::kWave;
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
@@ -1711,18 +1755,18 @@ void tgemm_skinny(KArgs a) {
   static_assert(kOut <= sk::kNT, "one quad per thread");
   if (tid < kOut) {
     const int m = tid / kQuads, cq = tid % kQuads;
-    v4i s = red[m * L::kPitch + cq];
+    v4i sum = red[m * L::kPitch + cq];
 #pragma unroll
-    for (int w = 1; w < sk::kWaves; ++w) s += red[w * L::kWave + m * L::kPitch + cq];
+    for (int w = 1; w < sk::kWaves; ++w) sum += red[w * L::kWave + m * L::kPitch + cq];
     const int32_t col = n0 + 4 * cq;
     if (m < a.M) {
       const float rsc = row_scale(a.o, m);
       if (a.o.vec && col + 3 < a.N) {
-        put4(a.o, a.N, m, col, s, rsc);
+        put4(a.o, a.N, m, col, sum, rsc);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (col + e < a.N) put1(a.o, a.N, m, col + e, s[e], rsc);
+          if (col + e < a.N) put1(a.o, a.N, m, col + e, sum[e], rsc);
       }
     }
   }
@@ -1782,9 +1826,11 @@ StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
 // The skinny forward: at most 32 rows, K % 64 == 0 (whole 64-steps, packed
 // rows in whole 16-byte pieces), 16-byte aligned A and Wpacked.  Column
 // blocks of 64, 32 or 16: the widest that still gives 128 workgroups or more
-// (A is re-read by every workgroup, so wider blocks read fewer bytes).
+// (A is re-read by every workgroup, so wider blocks read fewer bytes).  A in
+// whole lines through LDS above 8 rows (at 1 row it measured 5% slower, at
+// 16 and more 13-20% faster).
 struct SkinnyPlan {
-  bool ok;
+  bool ok, al;
   int32_t mf, nb, grid, lds;
 };
 
@@ -1794,16 +1840,18 @@ SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
   if (N > INT32_MAX - 64 || K > INT32_MAX) return kp;
   kp.mf = M > 16 ? 2 : 1;
   kp.nb = N >= 128 * 64 ? 4 : N >= 128 * 32 ? 2 : 1;
+  kp.al = M > 8;
   kp.grid = (int32_t)ceil_div(N, 16 * kp.nb);
-  kp.lds = sk::kWaves * 16 * kp.mf * (4 * kp.nb + 1) * 16;
+  const int32_t red = sk::kWaves * 16 * kp.mf * (4 * kp.nb + 1) * 16;
+  const int32_t tiles = kp.al ? sk::kWaves * 16 * kp.mf * 256 : 0;
+  kp.lds = red > tiles ? red : tiles;
   kp.ok = true;
   return kp;
 }
 
-template <int MF, int NB>
+template <int MF, int NB, bool AL>
 void launch_skinny(const KArgs &ka, int grid, hipStream_t stream) {
-  static_assert(SkLds<MF, NB>::kBytes == sk::kWaves * 16 * MF * (4 * NB + 1) * 16, "plan LDS");
-  hipLaunchKernelGGL((tgemm_skinny<MF, NB>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
+  hipLaunchKernelGGL((tgemm_skinny<MF, NB, AL>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
 }
 
 int pick_kernel(int op, int tile, int64_t L) {
@@ -1901,15 +1949,20 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
       ka.K = (int32_t)K;
       ka.nfull = (int32_t)(K / sk::SK);
       ka.vq = (int32_t)(K % sk::SK / BK);
-      const int sel = 10 * kp.mf + kp.nb;
+      const int sel = 100 * kp.mf + 10 * kp.nb + (kp.al ? 1 : 0);
       switch (sel) {
-        case 11: launch_skinny<1, 1>(ka, kp.grid, stream); break;
-        case 12: launch_skinny<1, 2>(ka, kp.grid, stream); break;
-        case 14: launch_skinny<1, 4>(ka, kp.grid, stream); break;
-        case 21: launch_skinny<2, 1>(ka, kp.grid, stream); break;
-        case 22: launch_skinny<2, 2>(ka, kp.grid, stream); break;
-        default: launch_skinny<2, 4>(ka, kp.grid, stream); break;
+        case 110: launch_skinny<1, 1, false>(ka, kp.grid, stream); break;
+        case 120: launch_skinny<1, 2, false>(ka, kp.grid, stream); break;
+        case 140: launch_skinny<1, 4, false>(ka, kp.grid, stream); break;
+        case 111: launch_skinny<1, 1, true>(ka, kp.grid, stream); break;
+        case 121: launch_skinny<1, 2, true>(ka, kp.grid, stream); break;
+        case 141: launch_skinny<1, 4, true>(ka, kp.grid, stream); break;
+        case 211: launch_skinny<2, 1, true>(ka, kp.grid, stream); break;
+        case 221: launch_skinny<2, 2, true>(ka, kp.grid, stream); break;
+        default: launch_skinny<2, 4, true>(ka, kp.grid, stream); break;
       }
+      static_assert(SkLds<2, 4, true>::kBytes == 8 * 32 * 17 * 16 && SkLds<1, 1, true>::kBytes == 8 * 16 * 256,
+                    "plan LDS");
       return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
     }
   }
