@@ -218,3 +218,61 @@ def scale_output(acc, row_scale, col_scale, out: str) -> np.ndarray:
     if out == "bf16":
         return bf16_nearest_even(y)
     raise ValueError(f"out must be 'f32' or 'bf16', got {out!r}")
+
+
+# ---------------------------------------------------------------------------
+# The steps before the product.
+#
+# Packing the trainer's ternary weights: the stored format is the pages'
+# (2-bit codes, four per byte along K, one row of K/4 bytes per output column
+# n; codes 0, 1, 2 stand for 0, +1, -1 [P10425 "What this adds"; P10855 PR
+# body]); the pages leave wiring the trainer to it for later.  The reading
+# taken: the input is int8 [N][K] (row n holds output column n's weights, as a
+# linear layer stores them), and a weight's code is chosen by its sign:
+# 1 for w > 0, 2 for w < 0, 0 for w == 0, so {-1, 0, +1} map to their codes
+# and code 3 is never produced.
+#
+# Quantizing activations to int8: the pages give only where the scales go
+# (per row for the forward's A and dX's dC; per column of X and dY for dW
+# [P10855 PR body]).  The reading taken is the plain symmetric absmax rule,
+# in IEEE single precision with nearest-even rounding at each step:
+#     s = max|x| / 127          over the row (or column)
+#     q = clamp(rint(x / s), -127, 127)      (q = 0 where s == 0)
+# so that q * s approximates x and a scaled output is (acc * s_row) * s_col.
+# ---------------------------------------------------------------------------
+
+def ternary_codes(Wt) -> np.ndarray:
+    """Codes uint8 [N][K] of int8 weights [N][K]: 1 if w > 0, 2 if w < 0, else 0."""
+    w = np.asarray(Wt, dtype=np.int8)
+    return np.where(w > 0, 1, np.where(w < 0, 2, 0)).astype(np.uint8)
+
+
+def pack_weights(Wt) -> np.ndarray:
+    """Stored weights uint8 [N][K/4] of int8 weights [N][K] (codes by sign)."""
+    return pack(ternary_codes(Wt))
+
+
+def as_float32(X, kind: str) -> np.ndarray:
+    """Values of the quantizer's input as float32 ("f32": float32 array;
+    "bf16": bfloat16 bit patterns, uint16, widened exactly)."""
+    if kind == "f32":
+        return np.ascontiguousarray(X, dtype=np.float32)
+    if kind == "bf16":
+        b = np.ascontiguousarray(X, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return b.view(np.float32)
+    raise ValueError(kind)
+
+
+def quantize(X, kind: str, axis: str):
+    """Symmetric int8 quantization of X [R][C]: axis "rows" gives one scale per
+    row (scale float32 [R]), "cols" one per column (scale float32 [C]).
+    Returns (q int8 [R][C], scale)."""
+    x = as_float32(X, kind)
+    ax = {"rows": 1, "cols": 0}[axis]
+    amax = np.abs(x).max(axis=ax) if x.size else np.zeros(x.shape[1 - ax], np.float32)
+    s = (amax.astype(np.float32) / np.float32(127)).astype(np.float32)
+    sb = s[:, None] if axis == "rows" else s[None, :]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(x / sb)
+    q = np.where(sb > 0, np.clip(r, -127, 127), 0).astype(np.int8)
+    return q, s

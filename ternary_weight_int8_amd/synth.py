@@ -51,6 +51,8 @@ STREAM_CODES = 1
 STREAM_DC = 2
 STREAM_ROW_SCALE = 3
 STREAM_COL_SCALE = 4
+STREAM_X = 5            # floating-point activations (quantizer input)
+STREAM_TERNARY = 6      # the trainer's ternary weights (packer input)
 
 # elements generated per numpy pass; bounds the temporaries to a few hundred MB
 _CHUNK = 1 << 24
@@ -199,3 +201,35 @@ def positive_scales(seed: int, stream: int, n: int, lo: float = 2.0 ** -10, hi: 
 
 # the weight scale of the scaled forward and dX calls in tests and benchmarks
 W_SCALE = 0.0371
+
+
+def float_inputs(seed: int, stream: int, rows: int, cols: int, kind: str) -> np.ndarray:
+    """Finite floating-point inputs for the quantizer, drawn as bit patterns:
+    "f32" gives float32 [rows][cols], "bf16" the bfloat16 bit patterns as
+    uint16 [rows][cols].  Each element takes a random sign, a binary exponent
+    uniform over -8 .. 3 and a random mantissa; about one element in 256 is
+    +0 or -0.  (Bits only: no rounding takes place here.)"""
+    u = splitmix64(seed, stream, rows * cols)
+    sign = (u >> np.uint64(63)).astype(np.uint32)
+    e = ((((u >> np.uint64(32)) & np.uint64(0xFFFFFFFF)) * np.uint64(12)) >> np.uint64(32)).astype(np.uint32)
+    e = e + np.uint32(127 - 8)                     # biased exponent, 2^-8 .. 2^3
+    zero = (u & np.uint64(0xFF)) == 0
+    if kind == "f32":
+        mant = ((u >> np.uint64(8)) & np.uint64((1 << 23) - 1)).astype(np.uint32)
+        bits = (sign << np.uint32(31)) | (e << np.uint32(23)) | mant
+        bits = np.where(zero, sign << np.uint32(31), bits).astype(np.uint32)
+        return bits.view(np.float32).reshape(rows, cols)
+    if kind == "bf16":
+        mant = ((u >> np.uint64(8)) & np.uint64(0x7F)).astype(np.uint32)
+        bits = (sign << np.uint32(15)) | (e << np.uint32(7)) | mant
+        bits = np.where(zero, sign << np.uint32(15), bits)
+        return bits.astype(np.uint16).reshape(rows, cols)
+    raise ValueError(kind)
+
+
+def ternary_int8(seed: int, N: int, K: int) -> np.ndarray:
+    """The trainer's ternary weights int8 [N][K] (row n: the K weights of
+    output column n, the layout of a linear layer's weight), each uniform
+    over {-1, 0, +1}: a uniform draw over {0, 1, 2} minus one."""
+    u = splitmix64(seed, STREAM_TERNARY, N * K)
+    return (_u_to_code3(u).astype(np.int16) - 1).astype(np.int8).reshape(N, K)

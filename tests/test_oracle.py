@@ -374,3 +374,94 @@ def test_scaled_orientation_exact_case():
     big = np.array([[2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 31)]], dtype=np.int32)
     got = oracle.scale_output(big, np.ones(1, np.float32), np.float32(1.0), "f32")
     np.testing.assert_array_equal(got, np.array([[2.0 ** 24, 2.0 ** 24 + 4, -2.0 ** 31]], np.float32))
+
+
+# ---------------------------------------------------------------------------
+# packing the trainer's ternary weights (codes by sign) and the per-row /
+# per-column int8 quantizer (symmetric absmax, IEEE single precision)
+# ---------------------------------------------------------------------------
+
+def test_pack_weights_hand_bytes():
+    # row [+1, -1, 0, +1] -> codes 1, 2, 0, 1 -> 1 + (2 << 2) + (0 << 4) + (1 << 6) = 0x49;
+    # signs only: [127, -128, 5, 0] -> codes 1, 2, 1, 0 -> 0x19
+    Wt = np.array([[1, -1, 0, 1, 127, -128, 5, 0]], dtype=np.int8)
+    assert oracle.pack_weights(Wt).tolist() == [[0x49, 0x19]]
+
+
+def test_pack_weights_round_trip_through_the_page_decode():
+    # decoding the packed ternary weights with the pages' table gives them back
+    Wt = synth.ternary_int8(3, 37, 96)
+    assert set(np.unique(Wt).tolist()) == {-1, 0, 1}
+    np.testing.assert_array_equal(oracle.decode(oracle.pack_weights(Wt), 96), Wt)
+
+
+def test_pack_weights_is_sign_of_any_int8():
+    W = synth.uniform_int8(4, synth.STREAM_A, 19, 64)
+    np.testing.assert_array_equal(oracle.decode(oracle.pack_weights(W), 64), np.sign(W).astype(np.int8))
+    assert 3 not in oracle.unpack(oracle.pack_weights(W), 64)
+
+
+def test_quantize_integer_row_with_max_127_is_identity():
+    # max |x| = 127 gives s = 1 exactly, and integer values stay as they are
+    x = np.array([[127, -127, 3, 0, -64, 1], [-127, 5, 0, 0, 2, 126]], dtype=np.float32)
+    q, s = oracle.quantize(x, "f32", "rows")
+    assert s.tolist() == [1.0, 1.0]
+    np.testing.assert_array_equal(q, x.astype(np.int8))
+
+
+def test_quantize_ties_round_to_even():
+    x = np.array([[127, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 126.5]], dtype=np.float32)
+    q, s = oracle.quantize(x, "f32", "rows")
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [[127, 2, 4, -2, -4, 0, 0, 126]]
+
+
+def test_quantize_power_of_two_scaling_is_exact():
+    x = synth.float_inputs(5, synth.STREAM_X, 7, 33, "f32")
+    q, s = oracle.quantize(x, "f32", "rows")
+    for e in (-12, -1, 5):
+        q2, s2 = oracle.quantize(x * np.float32(2.0 ** e), "f32", "rows")
+        np.testing.assert_array_equal(q2, q)
+        np.testing.assert_array_equal(s2, s * np.float32(2.0 ** e))
+
+
+def test_quantize_zero_row_and_signs():
+    x = np.zeros((3, 8), dtype=np.float32)
+    x[1] = np.linspace(-3, 3, 8, dtype=np.float32)
+    x[2, 3] = -0.0
+    q, s = oracle.quantize(x, "f32", "rows")
+    assert s[0] == 0 and s[2] == 0 and not q[0].any() and not q[2].any()
+    qn, sn = oracle.quantize(-x, "f32", "rows")
+    np.testing.assert_array_equal(qn, -q)
+    np.testing.assert_array_equal(sn, s)
+
+
+def test_quantize_error_within_half_a_step():
+    # against float64: |q s - x| <= s / 2 plus the one rounding of x / s
+    x = synth.float_inputs(6, synth.STREAM_X, 64, 300, "f32")
+    q, s = oracle.quantize(x, "f32", "rows")
+    err = np.abs(q.astype(np.float64) * s[:, None].astype(np.float64) - x.astype(np.float64))
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 127 * 2.0 ** -23)).all()
+    # the largest magnitude of each row maps to +-127
+    i = np.abs(x).argmax(axis=1)
+    assert (np.abs(q[np.arange(64), i]) == 127).all()
+    # s is max|x| / 127 to within one rounding
+    assert np.allclose(s.astype(np.float64) * 127, np.abs(x).max(axis=1), rtol=2.0 ** -23, atol=0)
+
+
+def test_quantize_columns_are_rows_of_the_transpose():
+    x = synth.float_inputs(7, synth.STREAM_X, 45, 29, "f32")
+    qc, sc = oracle.quantize(x, "f32", "cols")
+    qr, sr = oracle.quantize(np.ascontiguousarray(x.T), "f32", "rows")
+    np.testing.assert_array_equal(qc, qr.T)
+    np.testing.assert_array_equal(sc, sr)
+
+
+def test_quantize_bf16_input_widening():
+    b = np.array([[0x3F80, 0xC000, 0x0000, 0x8000, 0x42FE]], dtype=np.uint16)   # 1, -2, 0, -0, 127
+    assert oracle.as_float32(b, "bf16").tolist() == [[1.0, -2.0, 0.0, -0.0, 127.0]]
+    q, s = oracle.quantize(b, "bf16", "rows")
+    assert s.tolist() == [1.0] and q.tolist() == [[1, -2, 0, 0, 127]]
+    xb = synth.float_inputs(8, synth.STREAM_X, 5, 40, "bf16")
+    np.testing.assert_array_equal(oracle.quantize(xb, "bf16", "rows")[0],
+                                  oracle.quantize(oracle.as_float32(xb, "bf16"), "f32", "rows")[0])

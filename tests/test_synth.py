@@ -79,3 +79,22 @@ def test_extreme_inputs_structure():
     u = synth.splitmix64(1, 0, 4 * 16, offset=4 * 16)
     np.testing.assert_array_equal(A[4:].reshape(-1).view(np.uint8),
                                   (u >> np.uint64(56)).astype(np.uint8))
+
+
+def test_float_inputs_ranges_and_determinism():
+    x = synth.float_inputs(1, synth.STREAM_X, 50, 64, "f32")
+    assert x.dtype == np.float32 and np.isfinite(x).all()
+    nz = np.abs(x[x != 0])
+    assert nz.min() >= 2.0 ** -8 and nz.max() < 2.0 ** 4
+    assert (x == 0).sum() > 0
+    np.testing.assert_array_equal(x, synth.float_inputs(1, synth.STREAM_X, 50, 64, "f32"))
+    b = synth.float_inputs(1, synth.STREAM_X, 50, 64, "bf16")
+    assert b.dtype == np.uint16
+    assert (((b >> 7) & 0xFF)[b & 0x7FFF != 0] >= 127 - 8).all()
+
+
+def test_ternary_int8_values():
+    w = synth.ternary_int8(2, 30, 200)
+    assert w.dtype == np.int8 and set(np.unique(w).tolist()) == {-1, 0, 1}
+    counts = np.bincount((w.astype(np.int16) + 1).ravel())
+    assert counts.min() > 0.3 * w.size / 3
