@@ -46,8 +46,14 @@ def kernel_work(name, M, N, K):
     return ops, byts
 
 
-def source_digest():
-    src = os.path.join(ROOT, "ternary_weight_int8_amd", "csrc", "ternary_gemm.hip")
+PREP_KERNELS = ("pack", "quantize_rows", "quantize_cols")
+
+
+def source_digest(kernel=None):
+    """sha256 of the source file that holds a kernel (the GEMM kernels'
+    file unless the kernel is one of the packer / quantizer's)."""
+    name = "prep.hip" if kernel in PREP_KERNELS else "ternary_gemm.hip"
+    src = os.path.join(ROOT, "ternary_weight_int8_amd", "csrc", name)
     with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
@@ -64,7 +70,7 @@ def recorded_traffic(kernel, workload_tag):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_digest():
+    if fields.get("kernel_source_sha256") != source_digest(kernel):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))

@@ -57,7 +57,9 @@ typedef enum tgemm_status {
     TGEMM_ERR_ALIAS = -5,  /* the output overlaps an input                       */
     TGEMM_ERR_HIP = -6,    /* the HIP runtime reported an error at launch        */
     TGEMM_ERR_KIND = -7    /* the output kind of a scaled call is not one of
-                              TGEMM_OUT_F32, TGEMM_OUT_BF16                    */
+                              TGEMM_OUT_F32, TGEMM_OUT_BF16, or the input kind
+                              of a quantizer call not TGEMM_IN_F32,
+                              TGEMM_IN_BF16                                   */
 } tgemm_status;
 
 /* Longest contraction for which every int32 result is exact whatever the
@@ -146,6 +148,49 @@ int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const fl
 int ternary_gemm_s8_dw_scaled(const int8_t *A, const int8_t *dC, const float *a_col_scale,
                               const float *dc_col_scale, void *dW, int out_kind,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * The steps before the product (the pages give the stored format and where
+ * the activation scales go; the rules below are the readings taken).
+ *
+ * Packing the trainer's ternary weights [P10425 "What this adds": code
+ * table; P10855 PR body: wiring the trainer is left for later]:
+ *     Wpacked[n][k/4] bits 2(k%4), 2(k%4)+1  <-  code of Wt[n][k]
+ * with code 1 for w > 0, 2 for w < 0, 0 for w == 0 (so {-1, 0, +1} map to
+ * their codes and code 3 is never written).
+ *   Wt       int8   [N][K]     (row n: the weights of output column n, the
+ *                               layout of a linear layer's weight; device)
+ *   Wpacked  uint8  [N][K/4]   (written, never read; device)
+ * Requires N, K >= 1 and K % 4 == 0 (TGEMM_ERR_PACK); an output overlapping
+ * the input returns TGEMM_ERR_ALIAS.
+ */
+int ternary_pack_weights(const int8_t *Wt, uint8_t *Wpacked, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Symmetric int8 quantization of activations, with one scale per row
+ * (ternary_quantize_rows: the forward's A and dX's dC) or per column
+ * (ternary_quantize_cols: dW's A and dC) [P10855 PR body, the host's
+ * scales: per row for dX, per column of X and dY for dW]:
+ *     s = max |x| / 127                       over the row or column
+ *     q = clamp(rint(x / s), -127, 127)       (q = 0 where s == 0)
+ * each step in IEEE single precision rounded to nearest even (rint: ties to
+ * even).  The scale is the one the scaled calls above take, so that
+ * q * s approximates x to within half a step.
+ *   X      [R][C] float32 (TGEMM_IN_F32) or bfloat16 bit patterns
+ *          (TGEMM_IN_BF16), finite values (device)
+ *   Q      int8  [R][C] (written; device)
+ *   scale  float [R] (rows) or [C] (cols) (written; device; the column
+ *          variant also uses it as its running maximum, so it must not be
+ *          read by other work until the call completes)
+ * A NULL pointer returns TGEMM_ERR_NULL, another input kind TGEMM_ERR_KIND,
+ * R or C < 1 TGEMM_ERR_DIM, overlapping buffers TGEMM_ERR_ALIAS.
+ */
+#define TGEMM_IN_F32 1
+#define TGEMM_IN_BF16 2
+int ternary_quantize_rows(const void *X, int in_kind, int8_t *Q, float *scale, int64_t R, int64_t C,
+                          hipStream_t stream);
+int ternary_quantize_cols(const void *X, int in_kind, int8_t *Q, float *scale, int64_t R, int64_t C,
+                          hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *ternary_gemm_status_str(int status);

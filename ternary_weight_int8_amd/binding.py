@@ -14,6 +14,7 @@ from .build import LIB
 OK = 0
 ERR_NULL, ERR_DIM, ERR_PACK, ERR_BOUND, ERR_ALIAS, ERR_HIP, ERR_KIND = -1, -2, -3, -4, -5, -6, -7
 OUT_F32, OUT_BF16 = 1, 2   # output kinds of the scaled calls
+IN_F32, IN_BF16 = 1, 2     # input kinds of the quantizer calls
 
 # entry points declared in include/ternary_gemm.h
 EXPORTS = (
@@ -26,6 +27,9 @@ EXPORTS = (
     "ternary_gemm_s8_scaled",
     "ternary_gemm_s8_dx_scaled",
     "ternary_gemm_s8_dw_scaled",
+    "ternary_pack_weights",
+    "ternary_quantize_rows",
+    "ternary_quantize_cols",
 )
 
 OPS = {"fwd": 0, "dx": 1, "dw": 2}
@@ -83,6 +87,12 @@ def lib():
             f.restype = ctypes.c_int
         L.ternary_gemm_s8_dw_scaled.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
         L.ternary_gemm_s8_dw_scaled.restype = ctypes.c_int
+        L.ternary_pack_weights.argtypes = [p, p, i64, i64, p]
+        L.ternary_pack_weights.restype = ctypes.c_int
+        for name in ("ternary_quantize_rows", "ternary_quantize_cols"):
+            f = getattr(L, name)
+            f.argtypes = [p, i32, p, p, i64, i64, p]
+            f.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -299,3 +309,49 @@ def ternary_gemm_s8_dw_scaled(A, dC, a_col_scale, dc_col_scale, out_dtype=None, 
     if st != OK:
         raise TernaryGemmError("ternary_gemm_s8_dw_scaled", st, status_str(st))
     return dW
+
+
+# ---------------------------------------------------------------------------
+# the steps before the product: packing the trainer's ternary weights, and
+# per-row / per-column int8 quantization of activations
+# ---------------------------------------------------------------------------
+
+def ternary_pack_weights(Wt, Wpacked=None, stream=None):
+    """Wpacked uint8 [N][K/4] from int8 weights Wt [N][K] (codes by sign)."""
+    torch = _torch()
+    _check(Wt, torch.int8, 2, "Wt")
+    N, K = Wt.shape
+    Wpacked = _output(Wpacked, (N, K // 4), torch.uint8, Wt.device, "Wpacked")
+    st = lib().ternary_pack_weights(Wt.data_ptr(), Wpacked.data_ptr(), N, K, _stream(stream, Wt.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_pack_weights", st, status_str(st))
+    return Wpacked
+
+
+def _quantize(name, X, Q, scale, n_scale, stream):
+    torch = _torch()
+    if not isinstance(X, torch.Tensor) or X.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("X must be a float32 or bfloat16 torch.Tensor")
+    _check(X, X.dtype, 2, "X")
+    R, C = X.shape
+    Q = _output(Q, (R, C), torch.int8, X.device, "Q")
+    n = R if n_scale == "rows" else C
+    if scale is None:
+        scale = torch.empty((n,), dtype=torch.float32, device=X.device)
+    _scales(scale, n, "scale")
+    kind = IN_F32 if X.dtype == torch.float32 else IN_BF16
+    st = getattr(lib(), name)(X.data_ptr(), kind, Q.data_ptr(), scale.data_ptr(), R, C,
+                              _stream(stream, X.device))
+    if st != OK:
+        raise TernaryGemmError(name, st, status_str(st))
+    return Q, scale
+
+
+def ternary_quantize_rows(X, Q=None, scale=None, stream=None):
+    """(Q int8 [R][C], scale float32 [R]): per-row symmetric int8 quantization of X [R][C]."""
+    return _quantize("ternary_quantize_rows", X, Q, scale, "rows", stream)
+
+
+def ternary_quantize_cols(X, Q=None, scale=None, stream=None):
+    """(Q int8 [R][C], scale float32 [C]): per-column symmetric int8 quantization of X [R][C]."""
+    return _quantize("ternary_quantize_cols", X, Q, scale, "cols", stream)

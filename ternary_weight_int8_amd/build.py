@@ -7,6 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ternary_gemm.hip")
+SRCS = [SRC, os.path.join(PKG, "csrc", "prep.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libternary_gemm.so")
 ARCH = "gfx950"
@@ -17,7 +18,7 @@ def hipcc_cmd(out: str) -> list[str]:
         "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # no packed-fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, SRC, "-o", out,
+        "-I", INCLUDE, *SRCS, "-o", out,
     ]
 
 

@@ -315,3 +315,34 @@ def test_scaled_output_overlapping_a_scale_rejected():
                              M, N, K) == B.ERR_ALIAS
     # a bf16 output right after the row scales does not overlap them
     assert B.plan("fwd", M, N, K).out_rows == M
+
+
+# ---------------------------------------------------------------------------
+# packer and quantizer: argument checks (all on the host, before any launch)
+# ---------------------------------------------------------------------------
+
+def test_pack_weights_checks():
+    f = B.lib().ternary_pack_weights
+    a, b = 0x100000, 0x40000000
+    assert f(None, b, 4, 8, None) == B.ERR_NULL and f(a, None, 4, 8, None) == B.ERR_NULL
+    assert f(a, b, 0, 8, None) == B.ERR_DIM and f(a, b, 4, -4, None) == B.ERR_DIM
+    assert f(a, b, 4, 6, None) == B.ERR_PACK
+    assert f(a, a + 4 * 8 - 1, 4, 8, None) == B.ERR_ALIAS    # output ends inside the input
+    assert f(a, a - 4, 4, 8, None) == B.ERR_ALIAS            # output runs into the input
+
+
+@pytest.mark.parametrize("name", ["ternary_quantize_rows", "ternary_quantize_cols"])
+def test_quantize_checks(name):
+    f = getattr(B.lib(), name)
+    x, q, s = 0x100000, 0x20000000, 0x40000000
+    assert f(None, B.IN_F32, q, s, 4, 8, None) == B.ERR_NULL
+    assert f(x, B.IN_F32, None, s, 4, 8, None) == B.ERR_NULL
+    assert f(x, B.IN_F32, q, None, 4, 8, None) == B.ERR_NULL
+    for kind in (0, 3, -1):
+        assert f(x, kind, q, s, 4, 8, None) == B.ERR_KIND
+    assert f(x, B.IN_BF16, q, s, 0, 8, None) == B.ERR_DIM and f(x, B.IN_BF16, q, s, 4, 0, None) == B.ERR_DIM
+    # Q inside X (32 float32 = 128 bytes), the scale inside X or Q
+    assert f(x, B.IN_F32, x + 100, s, 4, 8, None) == B.ERR_ALIAS
+    assert f(x, B.IN_BF16, q, x + 60, 4, 8, None) == B.ERR_ALIAS
+    assert f(x, B.IN_F32, q, q + 30, 4, 8, None) == B.ERR_ALIAS
+    assert B.status_str(B.ERR_KIND).endswith("TGEMM_IN_BF16") or "kind" in B.status_str(B.ERR_KIND)
