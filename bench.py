@@ -196,6 +196,61 @@ def skinny_forward(B, synth, torch, stream, seed, steps):
     return out
 
 
+def prep_steps(B, synth, torch, stream, seed, steps):
+    """The steps before the product, each timed over `steps` launches on
+    inputs cycled through enough copies (more than 256 MB in all) that every
+    launch reads its input from HBM: packing ternary weights at 16384 x 16384
+    (the skinny workload's weights), and quantizing bf16 activations of the
+    step's shape (16384 x 1280) per row and per column.  Bytes: input read
+    once, outputs written once."""
+    dev = torch.device("cuda:0")
+    out = {}
+    cases = [
+        ("pack", "16384x16384", lambda: synth.ternary_int8(seed, 16384, 16384),
+         lambda x, o: B.ternary_pack_weights(x, Wpacked=o[0], stream=stream),
+         lambda x: (torch.empty((x.shape[0], x.shape[1] // 4), dtype=torch.uint8, device=dev),),
+         lambda R, C: R * C + R * C // 4),
+        ("quantize_rows", "16384x1280", lambda: synth.float_inputs(seed, synth.STREAM_X, 16384, 1280, "bf16"),
+         lambda x, o: B.ternary_quantize_rows(x, Q=o[0], scale=o[1], stream=stream),
+         lambda x: (torch.empty(x.shape, dtype=torch.int8, device=dev),
+                    torch.empty((x.shape[0],), dtype=torch.float32, device=dev)),
+         lambda R, C: 2 * R * C + R * C + 4 * R),
+        ("quantize_cols", "16384x1280", lambda: synth.float_inputs(seed, synth.STREAM_X, 16384, 1280, "bf16"),
+         lambda x, o: B.ternary_quantize_cols(x, Q=o[0], scale=o[1], stream=stream),
+         lambda x: (torch.empty(x.shape, dtype=torch.int8, device=dev),
+                    torch.empty((x.shape[1],), dtype=torch.float32, device=dev)),
+         lambda R, C: 2 * R * C + R * C + 4 * C),
+    ]
+    for name, tag, make, run, outs, nbytes in cases:
+        x = torch.from_numpy(make()).to(dev)
+        if x.dtype == torch.uint16:
+            x = x.view(torch.bfloat16)
+        R, C = x.shape
+        copies = max(2, -(-(512 << 20) // (x.numel() * x.element_size())))
+        xs = x.unsqueeze(0).repeat(copies, 1, 1)
+        o = outs(x)
+        for i in range(3):
+            run(xs[i % copies], o)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(steps):
+            run(xs[(i + 3) % copies], o)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t = ev0.elapsed_time(ev1) / steps / 1e3
+        byts = nbytes(R, C)
+        out[name] = {"workload": tag, "avg_us": t * 1e6, "gbps": byts / t / 1e9,
+                     "algorithmic_bytes": byts, "input_copies": copies,
+                     "roofline": {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM_BPS / 1e9,
+                                  "unit": "GB/s", "frac": byts / t / PEAK_HBM_BPS,
+                                  "traffic": recorded_traffic(name, tag)}}
+        del x, xs, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +267,9 @@ def main():
     ap.add_argument("--skinny-steps", type=int, default=50,
                     help="after the timed step, time the few-row forward (27 and 1 rows, cold "
                          "weights) over this many launches (0: skip)")
+    ap.add_argument("--prep-steps", type=int, default=50,
+                    help="after the timed step, time the packer and the quantizers over this many "
+                         "launches each (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -342,6 +400,8 @@ def main():
                                                 args.seed, args.scaled_steps)
     if args.skinny_steps > 0 and not args.only:
         line["skinny_forward"] = skinny_forward(B, synth, torch, stream, args.seed, args.skinny_steps)
+    if args.prep_steps > 0 and not args.only:
+        line["prep"] = prep_steps(B, synth, torch, stream, args.seed, args.prep_steps)
     if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:
         line["cpu_baseline"] = cpu_baseline(A, Wp, dC, K, min(args.cpu_rows, M))
     else:

@@ -124,6 +124,41 @@ __device__ __forceinline__ uint2 pack8(const float (&v)[8], float s) {
 
 constexpr int kQT = 256;   // threads per workgroup of the quantizer kernels
 
+// Per row, rows of at most 512 V elements on the vector path: one wave per
+// row (four per workgroup, grid-stride over rows), lane l holding units
+// l, l + 64, ... (8 elements each) in registers; max|x| across the wave with
+// xor shuffles, then q from the registers.  No LDS, no barrier.
+template <class T, int V>
+__global__ __launch_bounds__(256) void quant_rows_wave(const T *__restrict__ X, int8_t *__restrict__ Q,
+                                                       float *__restrict__ S, int64_t R, int64_t C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nu = C / 8;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < R; row += (int64_t)gridDim.x * 4) {
+    const T *x = X + row * C;
+    float v[V][8];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t u = lane + 64 * j;
+      if (u < nu) {
+        load8(x + 8 * u, v[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float s = __fdiv_rn(m, 127.f);
+    if (lane == 0) S[row] = s;
+    int8_t *q = Q + row * C;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t u = lane + 64 * j;
+      if (u < nu) *reinterpret_cast<uint2 *>(q + 8 * u) = pack8(v[j], s);
+    }
+  }
+}
+
 // Per row: one workgroup per row (grid-stride over rows).  Pass 1 takes
 // max|x| over the row (per thread, then across the wave with xor shuffles,
 // then across the four waves in LDS); s = max / 127; pass 2 reads the row
@@ -168,40 +203,146 @@ __global__ __launch_bounds__(kQT) void quant_rows(const T *__restrict__ X, int8_
   }
 }
 
-// Per column, in three launches: S = 0; each thread takes one column over a
-// run of rows, and raises S[col] to max|x| / 127 with an integer atomic max
-// on the float's bits (scales are >= +0, whose bit patterns order like their
-// values, and rounding x / 127 to nearest is monotone, so the largest
-// rounded quotient is the rounded quotient of the largest |x|; the result
-// does not depend on the order of the atomics); then q from S.
+// Per column.  A workgroup (four waves) takes a run of kRun rows and 512
+// columns, lane l columns 8 l .. 8 l + 7 of the block, wave w rows w, w + 4,
+// ... of the run; the four waves' maxima meet in LDS.  Each run's maxima go
+// to a partial row P[run][col] (float32), and a second kernel takes the max
+// over the runs (in run order; max is exact) and writes s = max / 127.  P
+// lives in Q's memory: ceil(R / kRun) x C floats take at most R x C bytes,
+// and the last kernel, which reads X and s and writes q, overwrites it.  With
+// a single run the first kernel writes s itself.  If Q is not 4-byte
+// aligned, the runs instead raise S[col] with an integer atomic max on the
+// float's bits (s >= +0, whose bit patterns order like their values, and
+// rounding max / 127 to nearest is monotone, so this gives the same s in any
+// order), after S is zeroed.
+constexpr int kRun = 64;      // rows per workgroup of the column kernels
+constexpr int kBatch = 8;     // loads issued together per thread
+constexpr int kColBlk = 512;  // columns per workgroup of the column kernels
+
+template <class T>
+__device__ __forceinline__ void load8_cols(const T *row, int64_t c0, int64_t C, bool vec, float (&v)[8]) {
+  if (vec) {
+    load8(row + c0, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = c0 + i < C ? widen<T>(row[c0 + i]) : 0.f;
+  }
+}
+
 __global__ __launch_bounds__(kQT) void fill_zero(float *S, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kQT + threadIdx.x;
   if (i < n) S[i] = 0.f;
 }
 
-constexpr int kColRun = 64;   // rows per thread of the column-max kernel
-
+// mode 0: write the run's maxima to P; 1: write s (single run); 2: atomic max into S
 template <class T>
-__global__ __launch_bounds__(kQT) void col_max(const T *__restrict__ X, float *__restrict__ S, int64_t R, int64_t C) {
-  const int64_t col = (int64_t)blockIdx.x * kQT + threadIdx.x;
-  if (col >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kColRun;
-  const int64_t r1 = r0 + kColRun < R ? r0 + kColRun : R;
+__global__ __launch_bounds__(kQT) void col_max(const T *__restrict__ X, float *__restrict__ P, float *__restrict__ S,
+                                               int64_t R, int64_t C, int vec, int mode) {
+  __shared__ float part[4][kColBlk];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kColBlk + 8 * lane;
+  const int64_t r0 = (int64_t)blockIdx.y * kRun;
+  const int64_t r1 = r0 + kRun < R ? r0 + kRun : R;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < C)
+    // eight rows per batch, their loads issued together; rows past the run
+    // repeat the run's last row (the max does not change)
+    for (int64_t rb = r0 + w; rb < r1; rb += 4 * kBatch) {
+      float v[kBatch][8];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t r = rb + 4 * k < r1 ? rb + 4 * k : r1 - 1;
+        load8_cols(X + r * C, c0, C, vec, v[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[k][i]));
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[w][8 * lane + i] = m[i];
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x + kQT * h;
+    const int64_t col = (int64_t)blockIdx.x * kColBlk + c;
+    if (col >= C) continue;
+    const float mx = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+    if (mode == 0) {
+      P[blockIdx.y * C + col] = mx;
+    } else {
+      const float s = __fdiv_rn(mx, 127.f);
+      if (mode == 1) S[col] = s;
+      else if (s > 0.f) atomicMax(reinterpret_cast<int *>(S + col), __float_as_int(s));
+    }
+  }
+}
+
+// max over the runs' partial rows: a workgroup takes 16 columns, its 16
+// run-groups of 16 threads each take every 16th run, and meet in LDS
+__global__ __launch_bounds__(kQT) void col_reduce(const float *__restrict__ P, float *__restrict__ S, int64_t runs,
+                                                  int64_t C) {
+  __shared__ float part[16][16];
+  const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int64_t col = (int64_t)blockIdx.x * 16 + c;
   float m = 0.f;
-  for (int64_t r = r0; r < r1; ++r) m = fmaxf(m, fabsf(widen<T>(X[r * C + col])));
-  const float s = __fdiv_rn(m, 127.f);
-  if (s > 0.f) atomicMax(reinterpret_cast<int *>(S + col), __float_as_int(s));
+  if (col < C)
+    for (int64_t rb = g; rb < runs; rb += 16 * kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t r = rb + 16 * k < runs ? rb + 16 * k : runs - 1;
+        t[k] = P[r * C + col];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) m = fmaxf(m, t[k]);
+    }
+  part[g][c] = m;
+  __syncthreads();
+  if (g == 0 && col < C) {
+#pragma unroll
+    for (int j = 1; j < 16; ++j) m = fmaxf(m, part[j][c]);
+    S[col] = __fdiv_rn(m, 127.f);
+  }
 }
 
 template <class T>
 __global__ __launch_bounds__(kQT) void col_quant(const T *__restrict__ X, const float *__restrict__ S,
-                                                 int8_t *__restrict__ Q, int64_t R, int64_t C) {
-  const int64_t col = (int64_t)blockIdx.x * kQT + threadIdx.x;
-  if (col >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kColRun;
-  const int64_t r1 = r0 + kColRun < R ? r0 + kColRun : R;
-  const float s = S[col];
-  for (int64_t r = r0; r < r1; ++r) Q[r * C + col] = quant1(widen<T>(X[r * C + col]), s);
+                                                 int8_t *__restrict__ Q, int64_t R, int64_t C, int vec) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kColBlk + 8 * lane;
+  if (c0 >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.y * kRun;
+  const int64_t r1 = r0 + kRun < R ? r0 + kRun : R;
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = c0 + i < C ? S[c0 + i] : 0.f;
+  for (int64_t rb = r0 + w; rb < r1; rb += 4 * kBatch) {
+    float v[kBatch][8];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t r = rb + 4 * k < r1 ? rb + 4 * k : r1 - 1;
+      load8_cols(X + r * C, c0, C, vec, v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (rb + 4 * k >= r1) break;
+      int8_t *q = Q + (rb + 4 * k) * C + c0;
+      if (vec) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo |= (uint32_t)(uint8_t)quant1(v[k][i], s[i]) << (8 * i);
+          hi |= (uint32_t)(uint8_t)quant1(v[k][4 + i], s[4 + i]) << (8 * i);
+        }
+        *reinterpret_cast<uint2 *>(q) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (c0 + i < C) q[i] = quant1(v[k][i], s[i]);
+      }
+    }
+  }
 }
 
 constexpr int kGridCap = 8 * 1024;   // workgroups of the packer's grid-stride kernels
@@ -250,6 +391,21 @@ int ternary_quantize_rows(const void *X, int in_kind, int8_t *Q, float *scale, i
   if (st != TGEMM_OK) return st;
   const int esz = in_kind == TGEMM_IN_F32 ? 4 : 2;
   const int vec = (C % 8 == 0 && aligned(X, 8 * esz > 16 ? 16 : 8 * esz) && aligned(Q, 8)) ? 1 : 0;
+  const int64_t nu = C / 8;
+  if (vec && nu <= 64 * 8) {
+    // one wave per row, the row in registers: V units of 8 per lane
+    const int64_t gw = (R + 3) / 4;
+    const dim3 g((unsigned)(gw < 65536 * 8 ? gw : 65536 * 8));
+    const int V = nu <= 64 ? 1 : nu <= 128 ? 2 : nu <= 256 ? 4 : 8;
+#define QRW(TY, VV) hipLaunchKernelGGL((quant_rows_wave<TY, VV>), g, dim3(256), 0, stream, static_cast<const TY *>(X), Q, scale, R, C)
+    if (in_kind == TGEMM_IN_F32) {
+      if (V == 1) QRW(float, 1); else if (V == 2) QRW(float, 2); else if (V == 4) QRW(float, 4); else QRW(float, 8);
+    } else {
+      if (V == 1) QRW(uint16_t, 1); else if (V == 2) QRW(uint16_t, 2); else if (V == 4) QRW(uint16_t, 4); else QRW(uint16_t, 8);
+    }
+#undef QRW
+    return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+  }
   const unsigned g = (unsigned)(R < 65536 * 32 ? R : 65536 * 32);
   if (in_kind == TGEMM_IN_F32)
     hipLaunchKernelGGL(quant_rows<float>, dim3(g), dim3(kQT), 0, stream, static_cast<const float *>(X), Q, scale,
@@ -264,19 +420,32 @@ int ternary_quantize_cols(const void *X, int in_kind, int8_t *Q, float *scale, i
                           hipStream_t stream) {
   const int st = prep_check(X, in_kind, Q, scale, R, C, C);
   if (st != TGEMM_OK) return st;
-  const int64_t gx = (C + kQT - 1) / kQT, gy = (R + kColRun - 1) / kColRun;
-  if (gx > INT32_MAX || gy > 65535) return TGEMM_ERR_DIM;
-  const dim3 grid((unsigned)gx, (unsigned)gy);
-  hipLaunchKernelGGL(fill_zero, dim3((unsigned)gx), dim3(kQT), 0, stream, scale, C);
-  if (in_kind == TGEMM_IN_F32) {
-    const float *x = static_cast<const float *>(X);
-    hipLaunchKernelGGL(col_max<float>, grid, dim3(kQT), 0, stream, x, scale, R, C);
-    hipLaunchKernelGGL(col_quant<float>, grid, dim3(kQT), 0, stream, x, scale, Q, R, C);
-  } else {
-    const uint16_t *x = static_cast<const uint16_t *>(X);
-    hipLaunchKernelGGL(col_max<uint16_t>, grid, dim3(kQT), 0, stream, x, scale, R, C);
-    hipLaunchKernelGGL(col_quant<uint16_t>, grid, dim3(kQT), 0, stream, x, scale, Q, R, C);
+  const int esz = in_kind == TGEMM_IN_F32 ? 4 : 2;
+  const int vec = (C % 8 == 0 && aligned(X, 8 * esz > 16 ? 16 : 8 * esz) && aligned(Q, 8)) ? 1 : 0;
+  const int64_t gx = (C + kColBlk - 1) / kColBlk, runs = (R + kRun - 1) / kRun;
+  if (gx > INT32_MAX || runs > 65535) return TGEMM_ERR_DIM;
+  const dim3 grid((unsigned)gx, (unsigned)runs);
+  // partial maxima in Q's memory (runs * C floats <= R * C bytes) when Q is 4-byte aligned
+  const int mode = runs == 1 ? 1 : aligned(Q, 4) ? 0 : 2;
+  float *P = reinterpret_cast<float *>(Q);
+  if (mode == 2) {
+    const int64_t gz = (C + kQT - 1) / kQT;
+    hipLaunchKernelGGL(fill_zero, dim3((unsigned)gz), dim3(kQT), 0, stream, scale, C);
   }
+  if (in_kind == TGEMM_IN_F32)
+    hipLaunchKernelGGL(col_max<float>, grid, dim3(kQT), 0, stream, static_cast<const float *>(X), P, scale, R, C,
+                       vec, mode);
+  else
+    hipLaunchKernelGGL(col_max<uint16_t>, grid, dim3(kQT), 0, stream, static_cast<const uint16_t *>(X), P, scale, R,
+                       C, vec, mode);
+  if (mode == 0)
+    hipLaunchKernelGGL(col_reduce, dim3((unsigned)((C + 15) / 16)), dim3(kQT), 0, stream, P, scale, runs, C);
+  if (in_kind == TGEMM_IN_F32)
+    hipLaunchKernelGGL(col_quant<float>, grid, dim3(kQT), 0, stream, static_cast<const float *>(X), scale, Q, R, C,
+                       vec);
+  else
+    hipLaunchKernelGGL(col_quant<uint16_t>, grid, dim3(kQT), 0, stream, static_cast<const uint16_t *>(X), scale, Q,
+                       R, C, vec);
   return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
 

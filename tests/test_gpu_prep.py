@@ -171,3 +171,18 @@ def test_quantize_misaligned_output():
     b = host(buf)
     assert b[0] == 77 and b[-1] == 77
     assert_same(b[1:1 + R * C].reshape(R, C), oracle.quantize(X, "f32", "rows")[0], "misaligned")
+
+
+@pytest.mark.parametrize("R,C", [(300, 272), (130, 37)])
+def test_quantize_cols_misaligned_output(R, C):
+    # an int8 output that is not 4-byte aligned cannot hold the per-run
+    # partial maxima, so the column scales come from the atomic-max path
+    say(f"quantize cols misaligned {R}x{C}")
+    X = _input(R, C, "bf16")
+    buf = torch.full((R * C + 2,), 77, dtype=torch.int8, device=DEV)
+    Q, S = B.ternary_quantize_cols(_to_torch(X, "bf16"), Q=buf[1:1 + R * C].view(R, C))
+    b = host(buf)
+    q, s = oracle.quantize(X, "bf16", "cols")
+    assert b[0] == 77 and b[-1] == 77
+    assert_same(host(S).view(np.uint32), s.view(np.uint32), "column scales (atomic path)")
+    assert_same(b[1:1 + R * C].reshape(R, C), q, "cols misaligned")
