@@ -186,3 +186,23 @@ def test_quantize_cols_misaligned_output(R, C):
     assert b[0] == 77 and b[-1] == 77
     assert_same(host(S).view(np.uint32), s.view(np.uint32), "column scales (atomic path)")
     assert_same(b[1:1 + R * C].reshape(R, C), q, "cols misaligned")
+
+
+def test_grid_stride_paths():
+    # more 64-byte chunks than the packer's grid has threads (8192 x 256), and
+    # more rows than the row quantizer's grid has waves (524288 x 4): both
+    # kernels loop over the remainder
+    N, K = 8200, 16400
+    say(f"pack grid-stride {N}x{K}")
+    Wt = synth.ternary_int8(21, N, K)
+    assert N * K // 64 > 8192 * 256
+    assert_same(host(B.ternary_pack_weights(dev(Wt))), oracle.pack_weights(Wt), "pack grid-stride")
+    del Wt
+    R, C = 2_100_000, 8
+    say(f"quantize rows grid-stride {R}x{C}")
+    X = synth.float_inputs(22, synth.STREAM_X, R, C, "bf16")
+    assert R > 524288 * 4
+    Q, S = B.ternary_quantize_rows(_to_torch(X, "bf16"))
+    q, s = oracle.quantize(X, "bf16", "rows")
+    assert_same(host(S).view(np.uint32), s.view(np.uint32), "row scales grid-stride")
+    assert_same(host(Q), q, "rows grid-stride")
