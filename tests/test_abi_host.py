@@ -346,3 +346,18 @@ def test_quantize_checks(name):
     assert f(x, B.IN_BF16, q, x + 60, 4, 8, None) == B.ERR_ALIAS
     assert f(x, B.IN_F32, q, q + 30, 4, 8, None) == B.ERR_ALIAS
     assert B.status_str(B.ERR_KIND).endswith("TGEMM_IN_BF16") or "kind" in B.status_str(B.ERR_KIND)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    # the product path has no fallback: with the library absent, the first
+    # call raises instead of computing anything some other way
+    import importlib
+    from ternary_weight_int8_amd import binding as Bfresh
+    Bfresh = importlib.reload(Bfresh)
+    monkeypatch.setattr(Bfresh, "LIB", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(Bfresh, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        Bfresh.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        Bfresh.plan("fwd", 4, 4, 4)
+    importlib.reload(Bfresh)
