@@ -220,10 +220,12 @@ const char *ternary_gemm_status_str(int status);
                                   workgroup per CU, operands loaded straight
                                   into LDS                                    */
 #define TGEMM_KERNEL_SKINNY 4  /* forward with M <= 32, K % 64 == 0, 16-byte
-                                  aligned A and Wpacked: one 8-wave workgroup
-                                  per 16, 32 or 64 output columns and all M
-                                  rows, its waves splitting the contraction;
-                                  bound by reading the packed weights         */
+                                  aligned A and Wpacked; dX with M <= 32,
+                                  N % 64 == 0, K % 16 == 0, 16-byte aligned dC
+                                  and Wpacked aligned for its row loads: one
+                                  8-wave workgroup per 16, 32 or 64 output
+                                  columns and all M rows, its waves splitting
+                                  the contraction                             */
 
 typedef struct tgemm_plan {
     int64_t out_rows, out_cols, contraction;

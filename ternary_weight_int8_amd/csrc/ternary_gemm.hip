@@ -1666,6 +1666,45 @@ __device__ __forceinline__ void sk_step(v4i (&acc)[MF][NB], const v4i (&w)[NB], 
   }
 }
 
+// The skinny kernels' end: each wave's partial sums go to LDS (row
+// 16 mf + lane % 16, quad 4 nb + lane / 16 of the tile, rows padded by one
+// quad); thread t then sums quad t % (4 NB) of tile row t / (4 NB) over the
+// eight waves, in wave order, and stores it at output row m, columns
+// c0 + 4 (t % (4 NB)) .. + 3 of a row-major output with `width` columns:
+// neighbouring threads write neighbouring 16-byte pieces of one output row.
+template <int MF, int NB>
+__device__ __forceinline__ void sk_epilogue(int8_t *smem, const v4i (&acc)[MF][NB], const Out &o, int wave, int lane,
+                                            int tid, int32_t c0, int32_t M, int32_t width) {
+  constexpr int kPitch = 4 * NB + 1, kWave = 16 * MF * kPitch;
+  const int r = lane & 15, g = lane >> 4;
+  v4i *red = reinterpret_cast<v4i *>(smem);
+  v4i *mine = red + wave * kWave;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mine[(16 * mf + r) * kPitch + 4 * nb + g] = acc[mf][nb];
+  __syncthreads();
+  constexpr int kQuads = 4 * NB, kOut = 16 * MF * kQuads;
+  static_assert(kOut <= sk::kNT, "one quad per thread");
+  if (tid < kOut) {
+    const int m = tid / kQuads, cq = tid % kQuads;
+    v4i sum = red[m * kPitch + cq];
+#pragma unroll
+    for (int w = 1; w < sk::kWaves; ++w) sum += red[w * kWave + m * kPitch + cq];
+    const int32_t col = c0 + 4 * cq;
+    if (m < M) {
+      const float rsc = row_scale(o, m);
+      if (o.vec && col + 3 < width) {
+        put4(o, width, m, col, sum, rsc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < width) put1(o, width, m, col + e, sum[e], rsc);
+      }
+    }
+  }
+}
+
 template <int MF, int NB, bool AL>
 __global__ __attribute__((amdgpu_flat_work_group_size(sk::kNT, sk::kNT), amdgpu_waves_per_eu(2)))
 void tgemm_skinny(KArgs a) {
@@ -1737,39 +1776,132 @@ void tgemm_skinny(KArgs a) {
     sk_step<MF, NB, AL>(acc, w, x, tile, lane);
   }
 
-  // partial sums -> LDS (row 16 mf + lane % 16, quad 4 nb + lane / 16 of the
-  // tile); with AL the buffer reuses the A tiles, once every wave is done
+  // partial sums -> LDS; with AL the buffer reuses the A tiles, once every
+  // wave is done with them
   if constexpr (AL) __syncthreads();
-  v4i *red = reinterpret_cast<v4i *>(smem);
-  v4i *mine = red + wave * L::kWave;
+  sk_epilogue<MF, NB>(smem, acc, a.o, wave, lane, tid, n0, a.M, a.N);
+}
+
+// ---------------------------------------------------------------------------
+// Skinny dX kernel (tgemm_skinny_dx): dX[M][K] = dC x W^T with at most 32
+// rows [P10855 PR body, kernel 1; the pages run it at 27 rows, "Measured"].
+// A workgroup of 8 waves owns BK = 16 NB output columns (contraction index k
+// of the forward) and all the rows; its waves split the contraction n into
+// steps of 64 (wave w takes steps w, w + 8, ...), and the partial sums are
+// added in LDS in wave order (sk_epilogue).  Per step each lane loads, a step
+// ahead, the 4 NB packed bytes (16 NB codes) of W row n = 64 s + lane for the
+// block's columns, and 16 bytes of dC row 16 mf + lane % 16 at n = 64 s +
+// 16 g.  The codes are decoded (decode16) into a wave-private LDS tile with
+// one row per contraction index (RowLayout<16 NB>), and the weight fragments
+// are read from it with the transposing read (TrRead), which yields the byte
+// order of a plain 16-byte dC read, so the two pair in one MFMA.  N % 64 == 0
+// (whole steps) and K % (16 NB) == 0 (whole column blocks): nothing is ragged
+// but the rows, which past M load the last row (computed, never stored).
+// ---------------------------------------------------------------------------
+struct XArgs {
+  const int8_t *dC;
+  const uint8_t *Wp;
+  Out o;              // column scale, when scaled: o.cscal (o.cs is null)
+  int32_t M, N, K;
+  int32_t nsteps;     // N / 64
+};
+
+template <int NB>
+struct SkW;   // a lane's packed bytes of one W row: 4 NB bytes
+template <>
+struct SkW<1> {
+  typedef uint32_t T;
+  __device__ __forceinline__ static uint32_t dw(const T &v, int) { return v; }
+};
+template <>
+struct SkW<4> {
+  typedef v4i T;
+  __device__ __forceinline__ static uint32_t dw(const T &v, int c) { return (uint32_t)v[c]; }
+};
+
+template <int MF, int NB>
+__device__ __forceinline__ void skx_load(typename SkW<NB>::T &w, v4i (&x)[MF], const uint8_t *wl,
+                                         const int8_t *const (&cl)[MF], int64_t wo, int64_t co) {
+  w = *reinterpret_cast<const typename SkW<NB>::T *>(wl + wo);
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) x[mf] = *reinterpret_cast<const v4i *>(cl[mf] + co);
+}
+
+template <int MF, int NB>
+__device__ __forceinline__ void skx_step(v4i (&acc)[MF][NB], const typename SkW<NB>::T &w, const v4i (&x)[MF],
+                                         int8_t *tile, int lane) {
+  typedef RowLayout<16 * NB> Lay;
+  // row `lane` of the tile: the decoded weights of contraction index 64 s + lane
+#pragma unroll
+  for (int c = 0; c < NB; ++c) *reinterpret_cast<v4i *>(tile + Lay::at(lane, c)) = decode16(SkW<NB>::dw(w, c));
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const v4i fw = TrRead::frag(tile + TrRead::off<Lay>(c, lane), 8 * 16 * NB);
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+      acc[mf][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw, x[mf], acc[mf][c], 0, 0, 0);
+  }
+}
+
+template <int MF, int NB>
+struct SkxLds {
+  static constexpr int kTile = RowLayout<16 * NB>::kBytes;
+  static constexpr int kRed = sk::kWaves * 16 * MF * (4 * NB + 1) * 16;
+  static constexpr int kTiles = sk::kWaves * kTile;
+  static constexpr int kBytes = kRed > kTiles ? kRed : kTiles;
+  static_assert(kBytes <= 80 * 1024, "two workgroups per CU");
+};
+
+template <int MF, int NB>
+__global__ __attribute__((amdgpu_flat_work_group_size(sk::kNT, sk::kNT), amdgpu_waves_per_eu(2)))
+void tgemm_skinny_dx(XArgs a) {
+  typedef SkxLds<MF, NB> L;
+  __shared__ __attribute__((aligned(256))) int8_t smem[L::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int32_t k0 = (int32_t)blockIdx.x * 16 * NB;
+  const int64_t kb = a.K / 4;
+  const uint8_t *wl = a.Wp + (int64_t)lane * kb + k0 / 4;       // row 64 s + lane: + 64 s kb
+  const int8_t *cl[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int32_t m = 16 * mf + r;
+    cl[mf] = a.dC + (int64_t)(m < a.M ? m : a.M - 1) * a.N + 16 * g;
+  }
+  int8_t *tile = smem + wave * L::kTile;
+  v4i acc[MF][NB];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) mine[(16 * mf + r) * L::kPitch + 4 * nb + g] = acc[mf][nb];
-  __syncthreads();
+    for (int c = 0; c < NB; ++c) acc[mf][c] = v4i{0, 0, 0, 0};
 
-  // thread t sums quad t % (4 NB) of tile row t / (4 NB) over the waves, in
-  // wave order, and stores it: neighbouring threads write neighbouring
-  // 16-byte pieces of one output row
-  constexpr int kQuads = 4 * NB, kOut = 16 * MF * kQuads;
-  static_assert(kOut <= sk::kNT, "one quad per thread");
-  if (tid < kOut) {
-    const int m = tid / kQuads, cq = tid % kQuads;
-    v4i sum = red[m * L::kPitch + cq];
-#pragma unroll
-    for (int w = 1; w < sk::kWaves; ++w) sum += red[w * L::kWave + m * L::kPitch + cq];
-    const int32_t col = n0 + 4 * cq;
-    if (m < a.M) {
-      const float rsc = row_scale(a.o, m);
-      if (a.o.vec && col + 3 < a.N) {
-        put4(a.o, a.N, m, col, sum, rsc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < a.N) put1(a.o, a.N, m, col + e, sum[e], rsc);
-      }
+  // the wave's steps wave + 8 i, i < cnt, two per iteration through two
+  // register sets, each load a step ahead (past the last step the load
+  // repeats it: in range, never used)
+  const int32_t cnt = a.nsteps > wave ? (a.nsteps - wave + sk::kWaves - 1) / sk::kWaves : 0;
+  if (cnt > 0) {
+    typename SkW<NB>::T w0, w1;
+    v4i x0[MF], x1[MF];
+    const int32_t last = wave + sk::kWaves * (cnt - 1);
+    const int64_t ws = 64 * kb;                                   // bytes of W per step
+    skx_load<MF, NB>(w0, x0, wl, cl, ws * wave, (int64_t)64 * wave);
+    int32_t s = wave;
+    for (int32_t i = 0; i + 2 <= cnt; i += 2) {
+      const int32_t s1 = s + sk::kWaves;
+      const int32_t s2 = s1 + sk::kWaves < last ? s1 + sk::kWaves : last;
+      skx_load<MF, NB>(w1, x1, wl, cl, ws * s1, (int64_t)64 * s1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      skx_step<MF, NB>(acc, w0, x0, tile, lane);
+      skx_load<MF, NB>(w0, x0, wl, cl, ws * s2, (int64_t)64 * s2);
+      __builtin_amdgcn_sched_barrier(0);
+      skx_step<MF, NB>(acc, w1, x1, tile, lane);
+      s += 2 * sk::kWaves;
     }
+    if (cnt & 1) skx_step<MF, NB>(acc, w0, x0, tile, lane);
   }
+  __syncthreads();   // the reduction buffer reuses the tiles
+  sk_epilogue<MF, NB>(smem, acc, a.o, wave, lane, tid, k0, a.M, a.K);
 }
 
 template <int OP, class T, bool FAST>
@@ -1847,6 +1979,31 @@ SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
   kp.lds = red > tiles ? red : tiles;
   kp.ok = true;
   return kp;
+}
+
+// The skinny dX: at most 32 rows, N % 64 == 0 (whole contraction steps),
+// K % 16 == 0, 16-byte aligned dC, and Wpacked aligned for the per-row
+// loads.  Column blocks of 64 (K % 64 == 0 and 128 or more of them) or 16.
+SkinnyPlan skinny_dx_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+  SkinnyPlan kp{};
+  if (op != DX || M > 32 || N % 64 != 0 || K % 16 != 0 || qalign % 16 != 0) return kp;
+  if (N > INT32_MAX || K > INT32_MAX - 64) return kp;
+  kp.mf = M > 16 ? 2 : 1;
+  kp.nb = (K % 64 == 0 && K / 64 >= 128) ? 4 : 1;
+  if (walign % (4 * kp.nb) != 0) return kp;
+  kp.al = false;
+  kp.grid = (int32_t)(K / (16 * kp.nb));
+  const int32_t red = sk::kWaves * 16 * kp.mf * (4 * kp.nb + 1) * 16;
+  const int32_t tiles = sk::kWaves * (kp.nb == 4 ? RowLayout<64>::kBytes : RowLayout<16>::kBytes);
+  kp.lds = red > tiles ? red : tiles;
+  kp.ok = true;
+  return kp;
+}
+
+template <int MF, int NB>
+void launch_skinny_dx(const XArgs &xa, int grid, hipStream_t stream) {
+  static_assert(SkxLds<MF, NB>::kTile == RowLayout<16 * NB>::kBytes, "plan LDS");
+  hipLaunchKernelGGL((tgemm_skinny_dx<MF, NB>), dim3(grid), dim3(sk::kNT), 0, stream, xa);
 }
 
 template <int MF, int NB, bool AL>
@@ -1967,6 +2124,24 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
   {
+    const SkinnyPlan kp = skinny_dx_plan(op, M, N, K, align_of(q), align_of(p));
+    if (kp.ok) {
+      XArgs xa;
+      xa.dC = q;
+      xa.Wp = static_cast<const uint8_t *>(p);
+      xa.o = o;
+      xa.M = (int32_t)M;
+      xa.N = (int32_t)N;
+      xa.K = (int32_t)K;
+      xa.nsteps = (int32_t)(N / BK);
+      if (kp.mf == 1)
+        kp.nb == 4 ? launch_skinny_dx<1, 4>(xa, kp.grid, stream) : launch_skinny_dx<1, 1>(xa, kp.grid, stream);
+      else
+        kp.nb == 4 ? launch_skinny_dx<2, 4>(xa, kp.grid, stream) : launch_skinny_dx<2, 1>(xa, kp.grid, stream);
+      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+    }
+  }
+  {
     const StreamPlan sp = stream_plan(op, M, N, K, align_of(q), align_of(p));
     if (sp.ok) {
       SArgs sa;
@@ -2072,7 +2247,8 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->contraction = s.L;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   {
-    const SkinnyPlan kp = skinny_plan(op, M, N, K, al, al);
+    SkinnyPlan kp = skinny_plan(op, M, N, K, al, al);
+    if (!kp.ok) kp = skinny_dx_plan(op, M, N, K, al, al);
     if (kp.ok) {
       plan->tile_rows = 16 * kp.mf;
       plan->tile_cols = 16 * kp.nb;

@@ -46,3 +46,10 @@ DX_STREAM_SHAPES = [(16300, 3456, 1296), (15000, 2048, 1424), (8192, 64, 5120), 
 SKINNY_SHAPES = [(1, 16, 64), (16, 100, 192), (17, 3456, 1280), (27, 3456, 1280), (27, 1280, 3456),
                  (32, 4099, 2112), (5, 8200, 4160), (1, 16384, 16384), (27, 16384, 16384),
                  (32, 65, 64), (2, 4096, 512), (31, 8256, 768)]
+
+# Shapes for the skinny dX kernel (M <= 32, contraction N % 64 == 0, K % 16
+# == 0): column blocks of 16 and 64, one and two 16-row blocks, fewer steps
+# than waves, the pages' 27-row backward at their weight shapes, and the
+# skinny workload's weights.
+SKINNY_DX_SHAPES = [(1, 64, 16), (16, 128, 48), (17, 640, 1296), (27, 3456, 1280), (27, 1280, 3456),
+                    (32, 192, 8192), (5, 8192, 8192), (27, 16384, 16384), (2, 4096, 4112), (31, 64, 8208)]

@@ -10,7 +10,8 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_SHAPES, STREAM_SHAPES, TILES
+from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
+                    STREAM_SHAPES, TILES)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -119,7 +120,7 @@ def _coverage(op, M, N, K):
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
     + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES]
-    + [("fwd",) + s for s in SKINNY_SHAPES])
+    + [("fwd",) + s for s in SKINNY_SHAPES] + [("dx",) + s for s in SKINNY_DX_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.lds_bytes <= 160 * 1024
@@ -140,10 +141,11 @@ def test_parity_shapes_reach_every_tile_and_path():
     # and every kernel on each load path it serves
     kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1),
                        (B.KERNEL_SKINNY, 1)},
-               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1)},
+               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1), (B.KERNEL_SKINNY, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES), ("dx", DX_SHAPES + DX_STREAM_SHAPES),
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES),
+                       ("dx", DX_SHAPES + DX_STREAM_SHAPES + SKINNY_DX_SHAPES),
                        ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
         for s in shapes:
@@ -177,7 +179,13 @@ def test_kernel_choice():
     assert B.plan("fwd", 33, 16384, 16384).kernel != B.KERNEL_SKINNY   # more than 32 rows
     assert B.plan("fwd", 27, 16384, 16352).kernel == B.KERNEL_TILED    # K % 64 != 0
     assert B.plan("fwd", 27, 16384, 16384, align=8).kernel == B.KERNEL_TILED
-    assert B.plan("dx", 27, 16384, 16384).kernel == B.KERNEL_TILED     # forward only
+    for s in SKINNY_DX_SHAPES:
+        assert B.plan("dx", *s).kernel == B.KERNEL_SKINNY, s
+    assert B.plan("dx", 27, 16384 + 32, 16384).kernel == B.KERNEL_TILED   # N % 64 != 0
+    assert B.plan("dx", 27, 16384, 16392).kernel == B.KERNEL_TILED        # K % 16 != 0
+    assert B.plan("dx", 33, 16384, 16384).kernel != B.KERNEL_SKINNY       # more than 32 rows
+    assert B.plan("dx", 27, 16384, 16384, align=8).kernel == B.KERNEL_TILED
+    assert B.plan("dw", 27, 16384, 16384).kernel != B.KERNEL_SKINNY
 
 
 def test_skinny_plan():
@@ -193,6 +201,16 @@ def test_skinny_plan():
         red, tiles = 8 * rows * (cols // 4 + 1) * 16, (8 * rows * 256 if M > 8 else 0)
         assert pl.lds_bytes == max(red, tiles)
         assert B.tile_of(pl, 3) == (0, 3 * cols)
+    # dX: column blocks of 64 (K % 64 == 0 and 128 or more blocks) or 16; the
+    # waves' tiles (64 contraction rows of the block's columns) share the
+    # memory of the reduction buffer
+    for (M, N, K), (rows, cols, tile) in {(27, 16384, 16384): (32, 64, 64 * 64), (5, 8192, 8192): (16, 64, 64 * 64),
+                                          (27, 3456, 1280): (32, 16, 64 * 16 + 256),
+                                          (1, 64, 4096): (16, 16, 64 * 16 + 256)}.items():
+        pl = B.plan("dx", M, N, K)
+        assert pl.kernel == B.KERNEL_SKINNY and (pl.tile_rows, pl.tile_cols) == (rows, cols), (M, N, K)
+        assert pl.tiles == pl.workgroups == K // cols
+        assert pl.lds_bytes == max(8 * rows * (cols // 4 + 1) * 16, 8 * tile)
 
 
 def test_tile_query_out_of_range():

@@ -14,7 +14,8 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
-from shapes import DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_SHAPES, STREAM_SHAPES
+from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
+                    STREAM_SHAPES)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -175,6 +176,14 @@ def test_fwd_skinny_shapes(M, N, K):
     assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd skinny {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", SKINNY_DX_SHAPES)
+def test_dx_skinny_shapes(M, N, K):
+    say(f"dx skinny {M}x{N}x{K} plan={tile_of('dx', M, N, K)}")
+    assert B.plan("dx", M, N, K).kernel == B.KERNEL_SKINNY
+    dC, Wp = synth.dx_inputs(M * 17 + N + K, M, N, K, 4)
+    assert_exact(gpu_dx(dC, Wp, K), oracle.dx(dC, Wp, K), f"dx skinny {M}x{N}x{K}")
+
+
 def test_skinny_extreme():
     # the int32 extremes through the skinny kernel: A row 0 all -128, row 1
     # uniform; codes +1 in columns < 16, -1 in the rest; K = 16777152, the
@@ -240,6 +249,7 @@ def test_misaligned_bases(offset):
 
 @pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 1900, 80),
                                       ("fwd", 27, 4099, 2112), ("dx", 299, 100, 268),
+                                      ("dx", 27, 640, 1296),
                                       ("dw", 97, 271, 299)])
 def test_writes_exactly_the_output(op, M, N, K):
     # the output sits between two canary bands inside one buffer, pre-filled
@@ -317,6 +327,8 @@ SCALED_CASES = [
     ("fwd", 5, 8200, 4160),       # skinny kernel, one 16-row block
     ("dx", 16300, 3456, 1296),    # stream dX, ragged rows and columns
     ("dx", 300, 96, 272),         # tiled dX
+    ("dx", 27, 3456, 1280),       # skinny dX, the pages' 27 rows
+    ("dx", 5, 8192, 8192),        # skinny dX, 64-column blocks, one 16-row block
     ("dw", 1090, 912, 4112),      # split dW kernel
     ("dw", 97, 271, 299),         # tiled dW, ragged
     ("dw", 16384, 3456, 1280),    # the timed shape
