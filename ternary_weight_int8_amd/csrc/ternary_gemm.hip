@@ -1713,7 +1713,8 @@ void tgemm_skinny(KArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int32_t n0 = (int32_t)blockIdx.x * 16 * NB;
+  // column block in the XCD-contiguous order (as the skinny dX kernel)
+  const int32_t n0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x) * 16 * NB;
   const int64_t kb = a.K / 4;
 
   const uint8_t *wr[NB];
@@ -1860,7 +1861,11 @@ void tgemm_skinny_dx(XArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int32_t k0 = (int32_t)blockIdx.x * 16 * NB;
+  // column block: each XCD (workgroup b runs on XCD b % 8) takes a
+  // contiguous run of blocks, so the blocks that share a 128-byte line of a
+  // packed row read it through one L2 (in the plain order, eight XCDs each
+  // fetched every line)
+  const int32_t k0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x) * 16 * NB;
   const int64_t kb = a.K / 4;
   const uint8_t *wl = a.Wp + (int64_t)lane * kb + k0 / 4;       // row 64 s + lane: + 64 s kb
   const int8_t *cl[MF];
@@ -2316,10 +2321,10 @@ int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iter
     tr = (int32_t)((start + pos) / tiles_c);
     tc = (int32_t)((start + pos) % tiles_c);
   } else if (plan->kernel == KSKINNY) {
-    // workgroup b: column block b, all rows
+    // all rows; the column block in the XCD-contiguous order
     if (iteration != 0) return TGEMM_ERR_DIM;
     tr = 0;
-    tc = (int32_t)workgroup;
+    tc = xcd_tile((int32_t)workgroup, tiles);
   } else {
     if (iteration != 0) return TGEMM_ERR_DIM;
     tile_rc(xcd_tile((int32_t)workgroup, tiles), tiles / tiles_c, tiles_c, plan->band_cols, &tr, &tc);

@@ -200,7 +200,10 @@ def test_skinny_plan():
         # above 8 rows the same memory first holds each wave's A tile (rows x 256 B)
         red, tiles = 8 * rows * (cols // 4 + 1) * 16, (8 * rows * 256 if M > 8 else 0)
         assert pl.lds_bytes == max(red, tiles)
-        assert B.tile_of(pl, 3) == (0, 3 * cols)
+        # the XCD-contiguous order: workgroup b (XCD b % 8) takes a run of blocks
+        q, r = divmod(pl.tiles, 8)
+        x, j = 3 % 8, 3 // 8
+        assert B.tile_of(pl, 3) == (0, (x * (q + 1) + j if x < r else r * (q + 1) + (x - r) * q + j) * cols)
     # dX: column blocks of 64 (K % 64 == 0 and 128 or more blocks) or 16; the
     # waves' tiles (64 contraction rows of the block's columns) share the
     # memory of the reduction buffer
