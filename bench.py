@@ -153,46 +153,54 @@ def scaled_outputs(B, synth, torch, stream, Ad, Wd, dCd, M, N, K, seed, steps):
 SKINNY = [(27, 16384, 16384), (1, 16384, 16384), (27, 3456, 1280)]
 
 
-def skinny_forward(B, synth, torch, stream, seed, steps):
-    """The forward with few rows (the skinny kernel, M <= 32; 27 is the
-    pages' backward batch), bound by reading the packed weights.  Successive
-    launches read different copies of the weights, more than 512 MB of them
-    in all, so that each launch streams its weights from HBM (past the
-    256 MB memory-side cache), as a pass over many layers would.  Bytes:
-    packed weights, activations, int32 output."""
+def skinny_rows(B, synth, torch, stream, seed, steps, op):
+    """The forward ("fwd") or dX ("dx") with few rows (the skinny kernels, M
+    <= 32; 27 is the pages' backward batch), bound by reading the packed
+    weights.  Successive launches read different copies of the weights, more
+    than 512 MB of them in all, so that each launch streams its weights from
+    HBM (past the 256 MB memory-side cache), as a pass over many layers
+    would.  Bytes: packed weights, the int8 rows, the int32 output."""
     out = {}
     dev = torch.device("cuda:0")
     for (M, N, K) in SKINNY:
-        A, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+        if op == "fwd":
+            X, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+            call = lambda Xd, W, O: B.ternary_gemm_s8(Xd, W, C=O, stream=stream)
+            shape, byts = (M, N), N * (K // 4) + M * K + 4 * M * N
+        else:
+            X, Wp = synth.dx_inputs(seed, M, N, K, 3)
+            call = lambda Xd, W, O: B.ternary_gemm_s8_dx(Xd, W, K, dX=O, stream=stream)
+            shape, byts = (M, K), N * (K // 4) + M * N + 4 * M * K
         copies = max(2, -(-(512 << 20) // (N * K // 4)))
-        Ad = torch.from_numpy(A).to(dev)
+        Xd = torch.from_numpy(X).to(dev)
         Ws = torch.from_numpy(Wp).to(dev).unsqueeze(0).repeat(copies, 1, 1)
-        C = torch.empty((M, N), dtype=torch.int32, device=dev)
-        first = B.ternary_gemm_s8(Ad, Ws[0], stream=stream).clone()
+        O = torch.empty(shape, dtype=torch.int32, device=dev)
+        first = torch.empty_like(O)
+        call(Xd, Ws[0], first)
         for i in range(3):
-            B.ternary_gemm_s8(Ad, Ws[i % copies], C=C, stream=stream)
+            call(Xd, Ws[i % copies], O)
         torch.cuda.synchronize()
-        if not torch.equal(first, C):
-            raise RuntimeError("skinny forward: copies of the same weights gave different results")
+        if not torch.equal(first, O):
+            raise RuntimeError(f"skinny {op}: copies of the same weights gave different results")
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for i in range(steps):
-            B.ternary_gemm_s8(Ad, Ws[(i + 3) % copies], C=C, stream=stream)
+            call(Xd, Ws[(i + 3) % copies], O)
         ev1.record(stream)
         torch.cuda.synchronize()
         t = ev0.elapsed_time(ev1) / steps / 1e3
         ops = 2 * M * N * K
-        byts = N * (K // 4) + M * K + 4 * M * N
         out[f"{M}x{N}x{K}"] = {"avg_us": t * 1e6, "gbps": byts / t / 1e9, "hbm_frac": byts / t / PEAK_HBM_BPS,
                                "tops": ops / t / 1e12, "algorithmic_bytes": byts, "ops": ops,
                                "weight_copies": copies}
-        del Ws, Ad, C, first
+        del Ws, Xd, O, first
         torch.cuda.empty_cache()
     head = out["27x16384x16384"]
+    kernel = "skinny" if op == "fwd" else "skinny_dx"
     out["roofline"] = {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                       "frac": head["hbm_frac"], "kernel": "skinny", "workload": "27x16384x16384",
-                       "traffic": recorded_traffic("skinny", "27x16384x16384")}
+                       "frac": head["hbm_frac"], "kernel": kernel, "workload": "27x16384x16384",
+                       "traffic": recorded_traffic(kernel, "27x16384x16384")}
     return out
 
 
@@ -265,8 +273,8 @@ def main():
                     help="after the timed step, time each product's scaled bf16 output "
                          "(the dequantizing epilogue) over this many launches (0: skip)")
     ap.add_argument("--skinny-steps", type=int, default=50,
-                    help="after the timed step, time the few-row forward (27 and 1 rows, cold "
-                         "weights) over this many launches (0: skip)")
+                    help="after the timed step, time the few-row forward and dX (27 and 1 rows, "
+                         "cold weights) over this many launches each (0: skip)")
     ap.add_argument("--prep-steps", type=int, default=50,
                     help="after the timed step, time the packer and the quantizers over this many "
                          "launches each (0: skip)")
@@ -399,7 +407,8 @@ def main():
         line["scaled_outputs"] = scaled_outputs(B, synth, torch, stream, Ad, Wd, dCd, M, N, K,
                                                 args.seed, args.scaled_steps)
     if args.skinny_steps > 0 and not args.only:
-        line["skinny_forward"] = skinny_forward(B, synth, torch, stream, args.seed, args.skinny_steps)
+        line["skinny_forward"] = skinny_rows(B, synth, torch, stream, args.seed, args.skinny_steps, "fwd")
+        line["skinny_dx"] = skinny_rows(B, synth, torch, stream, args.seed, args.skinny_steps, "dx")
     if args.prep_steps > 0 and not args.only:
         line["prep"] = prep_steps(B, synth, torch, stream, args.seed, args.prep_steps)
     if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:
