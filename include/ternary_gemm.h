@@ -22,7 +22,8 @@
  * Conventions shared by every call:
  *   - All matrix arguments are DEVICE pointers to dense row-major storage with
  *     no padding between rows; the caller owns them.  The library allocates,
- *     frees, copies and retains nothing.
+ *     frees, copies and retains nothing (the dX calls that take a workspace
+ *     borrow the caller's device memory for the duration of the call).
  *   - No alignment beyond the element size is required; aligned bases and
  *     row lengths that are multiples of 16 take the fast load path.
  *   - Each call validates its arguments on the host first.  On any error it
@@ -32,8 +33,10 @@
  *     and the call returns without waiting.  Faults that only show while the
  *     kernel runs surface at the caller's next synchronisation.
  *   - Results are exact: integer sums in int32, each output reduced over the
- *     whole contraction inside one workgroup in a fixed order (no split
- *     across workgroups, no atomics), so repeated calls give identical bits.
+ *     whole contraction in a fixed order with no atomics: inside one
+ *     workgroup, or, on the workspace path of dX, as per-workgroup partial
+ *     sums added in split order by a second kernel.  Integer addition is
+ *     exact, so every path and every repeated call gives identical bits.
  *   - Calls are thread-safe; concurrent calls on different streams may run at
  *     the same time as long as their outputs do not overlap.
  */
@@ -143,6 +146,40 @@ int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const fl
                               float w_scale, void *dX, int out_kind,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * dX with a workspace, for few rows and long rows of Wpacked (the backward
+ * of a decode-sized batch, [P10855 "Measured"]: 27 rows).  Same products,
+ * arguments, checks and results as ternary_gemm_s8_dx and
+ * ternary_gemm_s8_dx_scaled; in addition the caller lends `workspace`, a
+ * DEVICE buffer of `workspace_bytes` bytes.  When M <= 32, N % 64 == 0,
+ * K % 256 == 0, dC and Wpacked are 16-byte aligned and K / 256 column
+ * blocks are too few to fill the chip, the contraction is split across
+ * workgroups: each writes its int32 partial sums to the workspace and a
+ * second kernel adds them in split order, which is faster when each W row is
+ * long (27 x 16384 x 16384: 33 against 49 us).  The workspace must then hold
+ * ternary_gemm_dx_workspace() bytes and be 16-byte aligned; a NULL, smaller
+ * or unaligned workspace runs the one-pass kernels instead, with the same
+ * results.  The workspace's contents on entry do not matter and are garbage
+ * afterwards; it is in use until the call completes on `stream`, so calls
+ * that may overlap need workspaces of their own.  A workspace overlapping an
+ * input, the output or the scale vector returns TGEMM_ERR_ALIAS, a negative
+ * workspace_bytes TGEMM_ERR_DIM.
+ */
+int ternary_gemm_s8_dx_ws(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX,
+                          int64_t M, int64_t N, int64_t K, void *workspace,
+                          int64_t workspace_bytes, hipStream_t stream);
+int ternary_gemm_s8_dx_scaled_ws(const int8_t *dC, const uint8_t *Wpacked, const float *dc_row_scale,
+                                 float w_scale, void *dX, int out_kind,
+                                 int64_t M, int64_t N, int64_t K, void *workspace,
+                                 int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes the dX calls above use for these dimensions when the
+ * inputs' base alignment is `align` bytes (the smallest power-of-two
+ * alignment of dC and Wpacked; <= 0 counts as 1): written to *bytes, 0 when
+ * the one-pass kernels run anyway.  Returns TGEMM_OK, TGEMM_ERR_NULL for a
+ * NULL `bytes`, or the status a dX call would return for the dimensions. */
+int ternary_gemm_dx_workspace(int64_t M, int64_t N, int64_t K, int64_t align, int64_t *bytes);
+
 /* dW: Y[k][n] = (float(dW[k][n]) * a_col_scale[k]) * dc_col_scale[n];
  * a_col_scale float [K], dc_col_scale float [N]. */
 int ternary_gemm_s8_dw_scaled(const int8_t *A, const int8_t *dC, const float *a_col_scale,
@@ -206,8 +243,9 @@ const char *ternary_gemm_status_str(int status);
  * (vector-load) path applies given the base alignments passed in `align`
  * (the smallest power-of-two alignment of the input pointers, in bytes),
  * which kernel runs (TGEMM_KERNEL_*), and that kernel's threads and LDS bytes
- * per workgroup.  Returns TGEMM_OK, or the status the real call would return
- * for these dimensions (pointer checks excepted).
+ * per workgroup.  The plan is that of the calls without a workspace.
+ * Returns TGEMM_OK, or the status the real call would return for these
+ * dimensions (pointer checks excepted).
  */
 #define TGEMM_KERNEL_TILED 0   /* one 4-wave workgroup per output tile          */
 #define TGEMM_KERNEL_SPLIT 2   /* dW: the tile's contraction split between two

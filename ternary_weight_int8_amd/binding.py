@@ -30,6 +30,9 @@ EXPORTS = (
     "ternary_pack_weights",
     "ternary_quantize_rows",
     "ternary_quantize_cols",
+    "ternary_gemm_s8_dx_ws",
+    "ternary_gemm_s8_dx_scaled_ws",
+    "ternary_gemm_dx_workspace",
 )
 
 OPS = {"fwd": 0, "dx": 1, "dw": 2}
@@ -93,6 +96,12 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [p, i32, p, p, i64, i64, p]
             f.restype = ctypes.c_int
+        L.ternary_gemm_s8_dx_ws.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+        L.ternary_gemm_s8_dx_ws.restype = ctypes.c_int
+        L.ternary_gemm_s8_dx_scaled_ws.argtypes = [p, p, p, f32, p, i32, i64, i64, i64, p, i64, p]
+        L.ternary_gemm_s8_dx_scaled_ws.restype = ctypes.c_int
+        L.ternary_gemm_dx_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
+        L.ternary_gemm_dx_workspace.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -110,6 +119,15 @@ def call_raw_scaled(name: str, p0, p1, s0, s1, out, kind: int, M: int, N: int, K
     """Call a scaled entry point with raw addresses; s1 is the weight scale
     (a float) for the forward and dX, the dC column scales' address for dW."""
     return getattr(lib(), name)(p0, p1, s0, s1, out, kind, M, N, K, stream)
+
+
+def ternary_gemm_dx_workspace(M: int, N: int, K: int, align: int = 256) -> int:
+    """Workspace bytes the dX calls with a workspace use (0: the one-pass kernels run)."""
+    b = ctypes.c_int64()
+    st = lib().ternary_gemm_dx_workspace(M, N, K, align, ctypes.byref(b))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_dx_workspace", st, status_str(st))
+    return b.value
 
 
 def plan(op: str, M: int, N: int, K: int, align: int = 256):
@@ -202,6 +220,45 @@ def ternary_gemm_s8_dx(dC, Wpacked, K, dX=None, stream=None):
     return _invoke("ternary_gemm_s8_dx", dC, Wpacked, dX, M, N, K, stream)
 
 
+def _lowbit(addr: int) -> int:
+    return addr & -addr if addr else 1 << 20
+
+
+def _workspace(workspace, M, N, K, dC, Wpacked, stream):
+    """The caller's workspace (a contiguous uint8 device tensor), or a new one
+    of the size the library asks for; (address, bytes)."""
+    torch = _torch()
+    if workspace is None:
+        align = min(_lowbit(dC.data_ptr()), _lowbit(Wpacked.data_ptr()))
+        nbytes = ternary_gemm_dx_workspace(M, N, K, align)
+        if nbytes == 0:
+            return None, 0, None
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dC.device)
+        if stream is not None:
+            workspace.record_stream(stream)   # freed here, in use on `stream`
+    _check(workspace, torch.uint8, workspace.dim(), "workspace")
+    return workspace.data_ptr(), workspace.numel(), workspace
+
+
+def ternary_gemm_s8_dx_ws(dC, Wpacked, K, workspace=None, dX=None, stream=None):
+    """ternary_gemm_s8_dx with a workspace (a contiguous uint8 device tensor of
+    at least ternary_gemm_dx_workspace() bytes; None: one of that size is
+    allocated here)."""
+    torch = _torch()
+    _check(dC, torch.int8, 2, "dC")
+    _check(Wpacked, torch.uint8, 2, "Wpacked")
+    M, N = dC.shape
+    if tuple(Wpacked.shape) != (N, K // 4) or K % 4:
+        raise ValueError(f"Wpacked must be [N][K/4] = [{N}][{K // 4}], got {tuple(Wpacked.shape)}")
+    dX = _output(dX, (M, K), torch.int32, dC.device, "dX")
+    ws, nbytes, _keep = _workspace(workspace, M, N, K, dC, Wpacked, stream)
+    st = lib().ternary_gemm_s8_dx_ws(dC.data_ptr(), Wpacked.data_ptr(), dX.data_ptr(), M, N, K, ws, nbytes,
+                                     _stream(stream, dX.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_dx_ws", st, status_str(st))
+    return dX
+
+
 def ternary_gemm_s8_dw(A, dC, dW=None, stream=None):
     """dW int32 [K][N] = A^T x dC, A int8 [M][K], dC int8 [M][N]."""
     torch = _torch()
@@ -287,6 +344,27 @@ def ternary_gemm_s8_dx_scaled(dC, Wpacked, K, dc_row_scale, w_scale, out_dtype=N
                                          _stream(stream, dX.device))
     if st != OK:
         raise TernaryGemmError("ternary_gemm_s8_dx_scaled", st, status_str(st))
+    return dX
+
+
+def ternary_gemm_s8_dx_scaled_ws(dC, Wpacked, K, dc_row_scale, w_scale, out_dtype=None, workspace=None,
+                                 dX=None, stream=None):
+    """ternary_gemm_s8_dx_scaled with a workspace, as ternary_gemm_s8_dx_ws."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _check(dC, torch.int8, 2, "dC")
+    _check(Wpacked, torch.uint8, 2, "Wpacked")
+    M, N = dC.shape
+    if tuple(Wpacked.shape) != (N, K // 4) or K % 4:
+        raise ValueError(f"Wpacked must be [N][K/4] = [{N}][{K // 4}], got {tuple(Wpacked.shape)}")
+    _scales(dc_row_scale, M, "dc_row_scale")
+    dX = _output(dX, (M, K), out_dtype, dC.device, "dX")
+    ws, nbytes, _keep = _workspace(workspace, M, N, K, dC, Wpacked, stream)
+    st = lib().ternary_gemm_s8_dx_scaled_ws(dC.data_ptr(), Wpacked.data_ptr(), dc_row_scale.data_ptr(),
+                                            float(w_scale), dX.data_ptr(), _out_kind(out_dtype), M, N, K,
+                                            ws, nbytes, _stream(stream, dX.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_dx_scaled_ws", st, status_str(st))
     return dX
 
 

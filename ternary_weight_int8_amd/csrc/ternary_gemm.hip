@@ -1909,6 +1909,159 @@ void tgemm_skinny_dx(XArgs a) {
   sk_epilogue<MF, NB>(smem, acc, a.o, wave, lane, tid, k0, a.M, a.K);
 }
 
+// ---------------------------------------------------------------------------
+// Split skinny dX (tgemm_skinny_dx_split + skinny_dx_sum), the same product
+// as tgemm_skinny_dx for the same few rows, when the caller lends a
+// workspace.  What bounds tgemm_skinny_dx at long rows is the number of W
+// rows one load instruction touches: 64 rows of 16 bytes, each row in its own
+// page when K is large.  Here a workgroup owns 256 output columns, so a W row
+// contributes 64 contiguous bytes, and four neighbouring lanes load them:
+// one instruction covers 16 rows x 64 bytes.  With K / 256 column blocks too
+// few to fill the chip, the contraction n is split S ways across workgroups
+// (S column-block copies, each over a contiguous range of steps); each writes
+// its int32 partial sums to the workspace, and a second kernel adds the S
+// partials in split order and applies the output kind.  Integer addition is
+// exact, so the bits equal those of the one-pass kernels.
+//   Per step (64 contraction indices) a wave loads four 16-row slabs of W
+// (lane l: row 16 i + l / 4, bytes 16 (l % 4) .. + 15 of the block) and the
+// dC fragments as in tgemm_skinny_dx, decodes its 64 x 256 codes into a
+// wave-private LDS tile (RowLayout<256>: chunk 4 (l % 4) + j of row
+// 16 i + l / 4; a 16-lane pass then writes 16 distinct chunk slots) and reads
+// the 16 weight fragments back transposed.  The waves' partials meet in LDS
+// (one 16-row block at a time, 128 KB) and are stored as whole 16-byte
+// pieces.  Requirements (checked by the plan): M <= 32, N % 64 == 0,
+// K % 256 == 0, 16-byte aligned dC and Wpacked.
+// ---------------------------------------------------------------------------
+namespace sxs {
+constexpr int kBK = 256;                         // output columns per workgroup
+constexpr int kTile = RowLayout<kBK>::kBytes;    // 64 x 256 decoded codes
+constexpr int kLds = sk::kWaves * kTile;         // 128 KB: tiles, then the reduction
+}  // namespace sxs
+
+template <int MF>
+__device__ __forceinline__ void sxs_load(v4i (&w)[4], v4i (&x)[MF], const uint8_t *wl, int64_t kb,
+                                         const int8_t *const (&cl)[MF], int32_t st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const v4i *>(wl + ((int64_t)64 * st + 16 * i) * kb);
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) x[mf] = *reinterpret_cast<const v4i *>(cl[mf] + (int64_t)64 * st);
+}
+
+template <int MF>
+__device__ __forceinline__ void sxs_step(v4i (&acc)[MF][16], const v4i (&w)[4], const v4i (&x)[MF],
+                                         int8_t *tile, int lane) {
+  typedef RowLayout<sxs::kBK> Lay;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<v4i *>(tile + Lay::at(16 * i + (lane >> 2), 4 * (lane & 3) + j)) =
+          decode16((uint32_t)w[i][j]);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const v4i fw = TrRead::frag(tile + TrRead::off<Lay>(c, lane), 8 * sxs::kBK);
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+      acc[mf][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw, x[mf], acc[mf][c], 0, 0, 0);
+  }
+}
+
+template <int MF>
+__global__ __attribute__((amdgpu_flat_work_group_size(sk::kNT, sk::kNT), amdgpu_waves_per_eu(2)))
+void tgemm_skinny_dx_split(XArgs a, int32_t *part, int32_t S) {
+  __shared__ __attribute__((aligned(256))) int8_t smem[sxs::kLds];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  // the S splits of a column block are neighbours in the XCD-contiguous
+  // order, so they run on one XCD and share its L2 for dC
+  const int32_t b = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t blk = b / S, sp = b % S;
+  const int32_t k0 = blk * sxs::kBK;
+  const int64_t kb = a.K / 4;
+  const int32_t st0 = (int32_t)((int64_t)sp * a.nsteps / S);
+  const int32_t st1 = (int32_t)((int64_t)(sp + 1) * a.nsteps / S);
+  const uint8_t *wl = a.Wp + (int64_t)(lane >> 2) * kb + k0 / 4 + 16 * (lane & 3);
+  const int8_t *cl[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int32_t m = 16 * mf + r;
+    cl[mf] = a.dC + (int64_t)(m < a.M ? m : a.M - 1) * a.N + 16 * g;
+  }
+  int8_t *tile = smem + wave * sxs::kTile;
+  v4i acc[MF][16];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[mf][c] = v4i{0, 0, 0, 0};
+
+  // the wave's steps st0 + wave + 8 i < st1, two per iteration through two
+  // register sets, each load a step ahead (past the last step the load
+  // repeats it: in range, never used)
+  const int32_t first = st0 + wave;
+  const int32_t cnt = st1 > first ? (st1 - first + sk::kWaves - 1) / sk::kWaves : 0;
+  if (cnt > 0) {
+    v4i w0[4], w1[4], x0[MF], x1[MF];
+    const int32_t last = first + sk::kWaves * (cnt - 1);
+    sxs_load<MF>(w0, x0, wl, kb, cl, first);
+    int32_t st = first;
+    for (int32_t i = 0; i + 2 <= cnt; i += 2) {
+      const int32_t s1 = st + sk::kWaves;
+      const int32_t s2 = s1 + sk::kWaves < last ? s1 + sk::kWaves : last;
+      sxs_load<MF>(w1, x1, wl, kb, cl, s1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      sxs_step<MF>(acc, w0, x0, tile, lane);
+      sxs_load<MF>(w0, x0, wl, kb, cl, s2);
+      __builtin_amdgcn_sched_barrier(0);
+      sxs_step<MF>(acc, w1, x1, tile, lane);
+      st += 2 * sk::kWaves;
+    }
+    if (cnt & 1) sxs_step<MF>(acc, w0, x0, tile, lane);
+  }
+
+  // partials: the eight waves' sums of one 16-row block go to LDS as
+  // [wave][fragment][lane] (conflict-free 16-byte pieces), then thread t adds
+  // the eight copies of two (fragment, lane) pieces in wave order.  Lane l of
+  // fragment c holds row l % 16, columns 16 c + 4 (l / 16) .. + 3.
+  v4i *red = reinterpret_cast<v4i *>(smem);
+  int32_t *out = part + (int64_t)sp * a.M * a.K;
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    __syncthreads();   // the tiles (or the previous block's partials) are free
+#pragma unroll
+    for (int c = 0; c < 16; ++c) red[(wave * 16 + c) * 64 + lane] = acc[mf][c];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + sk::kNT * u, c = idx >> 6, ln = idx & 63;
+      v4i t = red[c * 64 + ln];
+#pragma unroll
+      for (int w = 1; w < sk::kWaves; ++w) t += red[(w * 16 + c) * 64 + ln];
+      const int32_t m = 16 * mf + (ln & 15);
+      if (m < a.M) *reinterpret_cast<v4i *>(out + (int64_t)m * a.K + k0 + 16 * c + 4 * (ln >> 4)) = t;
+    }
+  }
+}
+
+// dX = the sum of the S partials (split order), in the output kind; one
+// thread per 4 outputs (K % 256 == 0, so a row holds whole groups of 4).
+__global__ __launch_bounds__(256) void skinny_dx_sum(const v4i *__restrict__ part, Out o, int64_t M, int64_t K,
+                                                     int32_t S) {
+  const int64_t n4 = M * K / 4, kq = K / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    v4i t = part[i];
+    for (int32_t s = 1; s < S; ++s) t += part[(int64_t)s * n4 + i];
+    const int64_t row = i / kq, col = 4 * (i % kq);
+    const float rsc = row_scale(o, row);
+    if (o.vec) {
+      put4(o, K, row, col, t, rsc);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) put1(o, K, row, col + k, t[k], rsc);
+    }
+  }
+}
+
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -2005,6 +2158,33 @@ SkinnyPlan skinny_dx_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qal
   return kp;
 }
 
+// The split skinny dX (with a workspace): the skinny dX's rows, N % 64 == 0,
+// K % 256 == 0, 16-byte aligned dC and Wpacked; S = ceil(256 / (K / 256))
+// splits, so the grid fills the CUs once, at least two (K / 256 >= 256
+// column blocks fill the chip without a split, and the one-pass kernel runs)
+// and each wave with at least one step of every split (N / 64 >= 8 S).
+struct SplitDxPlan {
+  bool ok;
+  int32_t mf, blocks, S, grid;
+  int64_t bytes;      // workspace: S partial sums of M x K int32
+};
+SplitDxPlan skinny_dx_split_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+  SplitDxPlan xp{};
+  if (op != DX || M > 32 || N % 64 != 0 || K % sxs::kBK != 0 || qalign % 16 != 0 || walign % 16 != 0)
+    return xp;
+  if (N > INT32_MAX || K > INT32_MAX - 64) return xp;
+  const int64_t blocks = K / sxs::kBK, nsteps = N / 64;
+  const int64_t S = (256 + blocks - 1) / blocks;
+  if (S < 2 || nsteps < sk::kWaves * S) return xp;
+  xp.mf = M > 16 ? 2 : 1;
+  xp.blocks = (int32_t)blocks;
+  xp.S = (int32_t)S;
+  xp.grid = (int32_t)(blocks * S);
+  xp.bytes = S * M * K * 4;
+  xp.ok = true;
+  return xp;
+}
+
 template <int MF, int NB>
 void launch_skinny_dx(const XArgs &xa, int grid, hipStream_t stream) {
   static_assert(SkxLds<MF, NB>::kTile == RowLayout<16 * NB>::kBytes, "plan LDS");
@@ -2060,7 +2240,8 @@ hipError_t launch_op(const Args &a, int kernel, int tile, bool fast, hipStream_t
 // the scaled kinds (rs per output row; cs per output column, or null and
 // cscal for every column)
 int run(int op, const int8_t *q, const void *p, void *out, int kind, const float *rs, const float *cs,
-        float cscal, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+        float cscal, int64_t M, int64_t N, int64_t K, hipStream_t stream, void *ws = nullptr,
+        int64_t ws_bytes = 0) {
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
@@ -2073,6 +2254,10 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   if (overlaps(out, obytes, q, qbytes) || overlaps(out, obytes, p, pbytes)) return TGEMM_ERR_ALIAS;
   if (kind != OUT_I32 &&
       (overlaps(out, obytes, rs, s.R * 4) || (cs && overlaps(out, obytes, cs, s.Cc * 4))))
+    return TGEMM_ERR_ALIAS;
+  if (ws && ws_bytes > 0 &&
+      (overlaps(ws, ws_bytes, q, qbytes) || overlaps(ws, ws_bytes, p, pbytes) ||
+       overlaps(ws, ws_bytes, out, obytes) || (kind != OUT_I32 && overlaps(ws, ws_bytes, rs, s.R * 4))))
     return TGEMM_ERR_ALIAS;
   Out o;
   o.ptr = out;
@@ -2125,6 +2310,29 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
       }
       static_assert(SkLds<2, 4, true>::kBytes == 8 * 32 * 17 * 16 && SkLds<1, 1, true>::kBytes == 8 * 16 * 256,
                     "plan LDS");
+      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+    }
+  }
+  {
+    const SplitDxPlan xp = skinny_dx_split_plan(op, M, N, K, align_of(q), align_of(p));
+    if (xp.ok && ws && ws_bytes >= xp.bytes && aligned(ws, 16)) {
+      XArgs xa;
+      xa.dC = q;
+      xa.Wp = static_cast<const uint8_t *>(p);
+      xa.o = o;
+      xa.M = (int32_t)M;
+      xa.N = (int32_t)N;
+      xa.K = (int32_t)K;
+      xa.nsteps = (int32_t)(N / BK);
+      int32_t *part = static_cast<int32_t *>(ws);
+      if (xp.mf == 1)
+        hipLaunchKernelGGL((tgemm_skinny_dx_split<1>), dim3(xp.grid), dim3(sk::kNT), 0, stream, xa, part, xp.S);
+      else
+        hipLaunchKernelGGL((tgemm_skinny_dx_split<2>), dim3(xp.grid), dim3(sk::kNT), 0, stream, xa, part, xp.S);
+      if (hipGetLastError() != hipSuccess) return TGEMM_ERR_HIP;
+      const int64_t groups = ceil_div(M * K / 4, 256);
+      hipLaunchKernelGGL(skinny_dx_sum, dim3((uint32_t)(groups < 2048 ? groups : 2048)), dim3(256), 0, stream,
+                         reinterpret_cast<const v4i *>(part), o, M, K, xp.S);
       return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
     }
   }
@@ -2216,6 +2424,33 @@ int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const fl
   if (!dC || !Wpacked || !dc_row_scale || !dX) return TGEMM_ERR_NULL;
   if (out_kind != TGEMM_OUT_F32 && out_kind != TGEMM_OUT_BF16) return TGEMM_ERR_KIND;
   return run(DX, dC, Wpacked, dX, out_kind, dc_row_scale, nullptr, w_scale, M, N, K, stream);
+}
+
+int ternary_gemm_dx_workspace(int64_t M, int64_t N, int64_t K, int64_t align, int64_t *bytes) {
+  if (!bytes) return TGEMM_ERR_NULL;
+  const int st = check_dims(DX, M, N, K);
+  if (st != TGEMM_OK) return st;
+  const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
+  const SplitDxPlan xp = skinny_dx_split_plan(DX, M, N, K, al, al);
+  *bytes = xp.ok ? xp.bytes : 0;
+  return TGEMM_OK;
+}
+
+int ternary_gemm_s8_dx_ws(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX, int64_t M, int64_t N,
+                          int64_t K, void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (!dC || !Wpacked || !dX) return TGEMM_ERR_NULL;
+  if (workspace_bytes < 0) return TGEMM_ERR_DIM;
+  return run(DX, dC, Wpacked, dX, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream, workspace, workspace_bytes);
+}
+
+int ternary_gemm_s8_dx_scaled_ws(const int8_t *dC, const uint8_t *Wpacked, const float *dc_row_scale,
+                                 float w_scale, void *dX, int out_kind, int64_t M, int64_t N, int64_t K,
+                                 void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (!dC || !Wpacked || !dc_row_scale || !dX) return TGEMM_ERR_NULL;
+  if (out_kind != TGEMM_OUT_F32 && out_kind != TGEMM_OUT_BF16) return TGEMM_ERR_KIND;
+  if (workspace_bytes < 0) return TGEMM_ERR_DIM;
+  return run(DX, dC, Wpacked, dX, out_kind, dc_row_scale, nullptr, w_scale, M, N, K, stream, workspace,
+             workspace_bytes);
 }
 
 int ternary_gemm_s8_dw_scaled(const int8_t *A, const int8_t *dC, const float *a_col_scale,

@@ -53,3 +53,12 @@ SKINNY_SHAPES = [(1, 16, 64), (16, 100, 192), (17, 3456, 1280), (27, 3456, 1280)
 # skinny workload's weights.
 SKINNY_DX_SHAPES = [(1, 64, 16), (16, 128, 48), (17, 640, 1296), (27, 3456, 1280), (27, 1280, 3456),
                     (32, 192, 8192), (5, 8192, 8192), (27, 16384, 16384), (2, 4096, 4112), (31, 64, 8208)]
+
+# dX with a workspace, shapes that take the split kernel (M <= 32, N % 64 == 0,
+# K % 256 == 0, K / 256 < 256 column blocks): the pages' 27 rows at 16384^2
+# (4 splits), one row, one 16-row block with 8 splits, 17 rows with exactly one
+# step per wave and split, 32 rows with 16 splits, 256 splits of one column
+# block, splits of unequal length (33 and 100 steps over 4 and 6 splits; 300
+# workgroups)
+SPLIT_DX_SHAPES = [(27, 16384, 16384), (1, 16384, 16384), (16, 4096, 8192), (17, 2048, 16384),
+                   (32, 8192, 4096), (5, 131072, 256), (27, 2112, 16384), (3, 6400, 12800)]

@@ -3,6 +3,7 @@
 Validation runs before any HIP call, so every error path here is exercised
 without a device and without launching anything.
 """
+import ctypes
 import os
 import re
 
@@ -11,7 +12,7 @@ import pytest
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
 from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
-                    STREAM_SHAPES, TILES)
+                    SPLIT_DX_SHAPES, STREAM_SHAPES, TILES)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ternary_gemm.h")
@@ -382,3 +383,66 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="not built"):
         Bfresh.plan("fwd", 4, 4, 4)
     importlib.reload(Bfresh)
+
+
+# ---------------------------------------------------------------------------
+# dX with a workspace
+# ---------------------------------------------------------------------------
+
+def _splits(M, N, K):
+    blocks = K // 256
+    return -(-256 // blocks)
+
+
+def test_dx_workspace_size():
+    # S = ceil(256 / (K / 256)) splits of M x K int32 partials, for few rows,
+    # whole 64-row steps, 256-column blocks too few to fill the chip, every
+    # wave with a step in every split, and 16-byte aligned operands
+    assert B.ternary_gemm_dx_workspace(27, 16384, 16384) == 4 * 27 * 16384 * 4
+    assert B.ternary_gemm_dx_workspace(1, 16384, 16384) == 4 * 1 * 16384 * 4
+    assert B.ternary_gemm_dx_workspace(16, 4096, 8192) == 8 * 16 * 8192 * 4
+    assert B.ternary_gemm_dx_workspace(5, 131072, 256) == 256 * 5 * 256 * 4
+    assert B.ternary_gemm_dx_workspace(27, 3456, 1280) == 0       # 52 splits of 54 steps
+    assert B.ternary_gemm_dx_workspace(33, 16384, 16384) == 0     # more than 32 rows
+    assert B.ternary_gemm_dx_workspace(27, 16384 + 16, 16384) == 0
+    assert B.ternary_gemm_dx_workspace(27, 16384, 16384 + 64) == 0
+    assert B.ternary_gemm_dx_workspace(27, 16384, 65536) == 0     # 256 blocks: no split
+    assert B.ternary_gemm_dx_workspace(27, 16384, 16384, align=8) == 0
+    assert B.ternary_gemm_dx_workspace(27, 2048, 16384) > 0       # 32 steps: 8 per split
+    assert B.ternary_gemm_dx_workspace(27, 1984, 16384) == 0      # 31 steps
+    for M, N, K in SPLIT_DX_SHAPES:
+        assert B.ternary_gemm_dx_workspace(M, N, K) == _splits(M, N, K) * M * K * 4, (M, N, K)
+
+
+def test_dx_workspace_query_checks():
+    L, b = B.lib(), ctypes.c_int64(-1)
+    assert L.ternary_gemm_dx_workspace(27, 64, 256, 256, None) == B.ERR_NULL
+    assert L.ternary_gemm_dx_workspace(0, 64, 256, 256, ctypes.byref(b)) == B.ERR_DIM
+    assert L.ternary_gemm_dx_workspace(1, 64, 6, 256, ctypes.byref(b)) == B.ERR_PACK
+    tern = read_kv("bounds.txt")["ternary_max_contraction"]
+    assert L.ternary_gemm_dx_workspace(1, tern + 1, 4, 256, ctypes.byref(b)) == B.ERR_BOUND
+    assert b.value == -1                                          # untouched on error
+
+
+def test_dx_ws_checks():
+    # the plain dX call's checks, then the workspace's: a negative size is
+    # ERR_DIM, overlap with an input, the output or the row scales ERR_ALIAS;
+    # every case is refused on the host, before any launch
+    L = B.lib()
+    M, N, K = 27, 16384, 16384
+    dC, Wp, dX, rs, ws = 0x10000000, 0x20000000, 0x40000000, 0x50000000, 0x60000000
+    big = 1 << 24
+    f = L.ternary_gemm_s8_dx_ws
+    for args in ((None, Wp, dX), (dC, None, dX), (dC, Wp, None)):
+        assert f(*args, M, N, K, ws, big, None) == B.ERR_NULL
+    assert f(dC, Wp, dX, 0, N, K, ws, big, None) == B.ERR_DIM
+    assert f(dC, Wp, dX, M, N, 6, ws, big, None) == B.ERR_PACK
+    assert f(dC, Wp, dX, M, N, K, ws, -1, None) == B.ERR_DIM
+    for w in (dC + 64, Wp + N * K // 4 - 16, dX + 100, dX - big + 16):
+        assert f(dC, Wp, dX, M, N, K, w, big, None) == B.ERR_ALIAS, hex(w)
+    g = L.ternary_gemm_s8_dx_scaled_ws
+    assert g(dC, Wp, None, 1.0, dX, B.OUT_F32, M, N, K, ws, big, None) == B.ERR_NULL
+    assert g(dC, Wp, rs, 1.0, dX, 7, M, N, K, ws, big, None) == B.ERR_KIND
+    assert g(dC, Wp, rs, 1.0, dX, B.OUT_F32, M, N, K, ws, -5, None) == B.ERR_DIM
+    assert g(dC, Wp, rs, 1.0, dX, B.OUT_BF16, M, N, K, rs - 8, 64, None) == B.ERR_ALIAS
+    assert g(dC, Wp, rs, 1.0, dX, B.OUT_BF16, M, N, K, dX + M * K * 2 - 4, 64, None) == B.ERR_ALIAS
