@@ -159,22 +159,13 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
     weights.  Successive launches read different copies of the weights, more
     than 512 MB of them in all, so that each launch streams its weights from
     HBM (past the 256 MB memory-side cache), as a pass over many layers
-    would.  Bytes: packed weights, the int8 rows, the int32 output."""
+    would.  Bytes: packed weights, the int8 rows, the int32 output.  dX runs
+    with a workspace (the contraction split across workgroups where that
+    applies, two kernels per call); the one-pass call is timed beside it."""
     out = {}
     dev = torch.device("cuda:0")
-    for (M, N, K) in SKINNY:
-        if op == "fwd":
-            X, Wp = synth.fwd_inputs(seed, M, N, K, 3)
-            call = lambda Xd, W, O: B.ternary_gemm_s8(Xd, W, C=O, stream=stream)
-            shape, byts = (M, N), N * (K // 4) + M * K + 4 * M * N
-        else:
-            X, Wp = synth.dx_inputs(seed, M, N, K, 3)
-            call = lambda Xd, W, O: B.ternary_gemm_s8_dx(Xd, W, K, dX=O, stream=stream)
-            shape, byts = (M, K), N * (K // 4) + M * N + 4 * M * K
-        copies = max(2, -(-(512 << 20) // (N * K // 4)))
-        Xd = torch.from_numpy(X).to(dev)
-        Ws = torch.from_numpy(Wp).to(dev).unsqueeze(0).repeat(copies, 1, 1)
-        O = torch.empty(shape, dtype=torch.int32, device=dev)
+
+    def timed(call, Xd, Ws, O, copies):
         first = torch.empty_like(O)
         call(Xd, Ws[0], first)
         for i in range(3):
@@ -189,15 +180,41 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
             call(Xd, Ws[(i + 3) % copies], O)
         ev1.record(stream)
         torch.cuda.synchronize()
-        t = ev0.elapsed_time(ev1) / steps / 1e3
+        return ev0.elapsed_time(ev1) / steps / 1e3, first
+
+    for (M, N, K) in SKINNY:
+        one_pass = None
+        if op == "fwd":
+            X, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+            call = lambda Xd, W, O: B.ternary_gemm_s8(Xd, W, C=O, stream=stream)
+            shape, byts = (M, N), N * (K // 4) + M * K + 4 * M * N
+        else:
+            X, Wp = synth.dx_inputs(seed, M, N, K, 3)
+            nws = B.ternary_gemm_dx_workspace(M, N, K)
+            ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+            call = lambda Xd, W, O: B.ternary_gemm_s8_dx_ws(Xd, W, K, workspace=ws, dX=O, stream=stream)
+            one_pass = lambda Xd, W, O: B.ternary_gemm_s8_dx(Xd, W, K, dX=O, stream=stream)
+            shape, byts = (M, K), N * (K // 4) + M * N + 4 * M * K
+        copies = max(2, -(-(512 << 20) // (N * K // 4)))
+        Xd = torch.from_numpy(X).to(dev)
+        Ws = torch.from_numpy(Wp).to(dev).unsqueeze(0).repeat(copies, 1, 1)
+        O = torch.empty(shape, dtype=torch.int32, device=dev)
+        t, first = timed(call, Xd, Ws, O, copies)
         ops = 2 * M * N * K
-        out[f"{M}x{N}x{K}"] = {"avg_us": t * 1e6, "gbps": byts / t / 1e9, "hbm_frac": byts / t / PEAK_HBM_BPS,
-                               "tops": ops / t / 1e12, "algorithmic_bytes": byts, "ops": ops,
-                               "weight_copies": copies}
+        row = {"avg_us": t * 1e6, "gbps": byts / t / 1e9, "hbm_frac": byts / t / PEAK_HBM_BPS,
+               "tops": ops / t / 1e12, "algorithmic_bytes": byts, "ops": ops, "weight_copies": copies}
+        if one_pass is not None:
+            t1, first1 = timed(one_pass, Xd, Ws, O, copies)
+            if not torch.equal(first, first1):
+                raise RuntimeError(f"skinny dX {M}x{N}x{K}: the workspace and one-pass calls differ")
+            row["workspace_bytes"] = nws
+            row["kernels_per_call"] = 2 if nws else 1
+            row["one_pass_us"] = t1 * 1e6
+        out[f"{M}x{N}x{K}"] = row
         del Ws, Xd, O, first
         torch.cuda.empty_cache()
     head = out["27x16384x16384"]
-    kernel = "skinny" if op == "fwd" else "skinny_dx"
+    kernel = "skinny" if op == "fwd" else "skinny_dx_split"
     out["roofline"] = {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                        "frac": head["hbm_frac"], "kernel": kernel, "workload": "27x16384x16384",
                        "traffic": recorded_traffic(kernel, "27x16384x16384")}
