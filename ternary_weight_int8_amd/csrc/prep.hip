@@ -306,28 +306,37 @@ __global__ __launch_bounds__(kQT) void col_reduce(const float *__restrict__ P, f
   }
 }
 
+// q from X and s: a wave takes kQRows consecutive rows of the block's 512
+// columns, loading the 8 column scales of each lane once and all its rows'
+// inputs together, so one memory round trip serves the wave; many short
+// waves then hide the latency, as in the row kernel.  Row groups are
+// grid-strided past the grid's y limit.
+constexpr int kQRows = 4;                       // rows per wave of col_quant
+constexpr int kQGroup = 4 * kQRows;             // rows per workgroup of col_quant
+
 template <class T>
 __global__ __launch_bounds__(kQT) void col_quant(const T *__restrict__ X, const float *__restrict__ S,
                                                  int8_t *__restrict__ Q, int64_t R, int64_t C, int vec) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kColBlk + 8 * lane;
   if (c0 >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kRun;
-  const int64_t r1 = r0 + kRun < R ? r0 + kRun : R;
   float s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = c0 + i < C ? S[c0 + i] : 0.f;
-  for (int64_t rb = r0 + w; rb < r1; rb += 4 * kBatch) {
-    float v[kBatch][8];
+  const int64_t groups = (R + kQGroup - 1) / kQGroup;
+  for (int64_t gy = blockIdx.y; gy < groups; gy += gridDim.y) {
+    const int64_t r0 = gy * kQGroup + (int64_t)w * kQRows;
+    if (r0 >= R) break;
+    float v[kQRows][8];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int64_t r = rb + 4 * k < r1 ? rb + 4 * k : r1 - 1;
+    for (int k = 0; k < kQRows; ++k) {
+      const int64_t r = r0 + k < R ? r0 + k : R - 1;
       load8_cols(X + r * C, c0, C, vec, v[k]);
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      if (rb + 4 * k >= r1) break;
-      int8_t *q = Q + (rb + 4 * k) * C + c0;
+    for (int k = 0; k < kQRows; ++k) {
+      if (r0 + k >= R) break;
+      int8_t *q = Q + (r0 + k) * C + c0;
       if (vec) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -440,12 +449,14 @@ int ternary_quantize_cols(const void *X, int in_kind, int8_t *Q, float *scale, i
                        C, vec, mode);
   if (mode == 0)
     hipLaunchKernelGGL(col_reduce, dim3((unsigned)((C + 15) / 16)), dim3(kQT), 0, stream, P, scale, runs, C);
+  const int64_t qgroups = (R + kQGroup - 1) / kQGroup;
+  const dim3 qgrid((unsigned)gx, (unsigned)(qgroups < 65535 ? qgroups : 65535));
   if (in_kind == TGEMM_IN_F32)
-    hipLaunchKernelGGL(col_quant<float>, grid, dim3(kQT), 0, stream, static_cast<const float *>(X), scale, Q, R, C,
-                       vec);
+    hipLaunchKernelGGL(col_quant<float>, qgrid, dim3(kQT), 0, stream, static_cast<const float *>(X), scale, Q, R,
+                       C, vec);
   else
-    hipLaunchKernelGGL(col_quant<uint16_t>, grid, dim3(kQT), 0, stream, static_cast<const uint16_t *>(X), scale, Q,
-                       R, C, vec);
+    hipLaunchKernelGGL(col_quant<uint16_t>, qgrid, dim3(kQT), 0, stream, static_cast<const uint16_t *>(X), scale,
+                       Q, R, C, vec);
   return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
 

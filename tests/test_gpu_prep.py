@@ -206,3 +206,16 @@ def test_grid_stride_paths():
     q, s = oracle.quantize(X, "bf16", "rows")
     assert_same(host(S).view(np.uint32), s.view(np.uint32), "row scales grid-stride")
     assert_same(host(Q), q, "rows grid-stride")
+
+
+def test_quantize_cols_grid_stride():
+    # more 16-row groups than the column kernel's grid has in y (65535): its
+    # workgroups loop over the remainder
+    R, C = 1_100_000, 8
+    say(f"quantize cols grid-stride {R}x{C}")
+    assert -(-R // 16) > 65535
+    X = synth.float_inputs(23, synth.STREAM_X, R, C, "bf16")
+    Q, S = B.ternary_quantize_cols(_to_torch(X, "bf16"))
+    q, s = oracle.quantize(X, "bf16", "cols")
+    assert_same(host(S).view(np.uint32), s.view(np.uint32), "column scales grid-stride")
+    assert_same(host(Q), q, "cols grid-stride")
