@@ -237,13 +237,15 @@ def _workspace(workspace, M, N, K, dC, Wpacked, stream):
         if stream is not None:
             workspace.record_stream(stream)   # freed here, in use on `stream`
     _check(workspace, torch.uint8, workspace.dim(), "workspace")
+    if workspace.numel() == 0:
+        return None, 0, workspace
     return workspace.data_ptr(), workspace.numel(), workspace
 
 
 def ternary_gemm_s8_dx_ws(dC, Wpacked, K, workspace=None, dX=None, stream=None):
     """ternary_gemm_s8_dx with a workspace (a contiguous uint8 device tensor of
-    at least ternary_gemm_dx_workspace() bytes; None: one of that size is
-    allocated here)."""
+    at least ternary_gemm_dx_workspace() bytes, empty for none; None: one of
+    that size is allocated here)."""
     torch = _torch()
     _check(dC, torch.int8, 2, "dC")
     _check(Wpacked, torch.uint8, 2, "Wpacked")

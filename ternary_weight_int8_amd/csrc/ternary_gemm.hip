@@ -2045,12 +2045,22 @@ void tgemm_skinny_dx_split(XArgs a, int32_t *part, int32_t S) {
 
 // dX = the sum of the S partials (split order), in the output kind; one
 // thread per 4 outputs (K % 256 == 0, so a row holds whole groups of 4).
+// Eight partials are loaded before any is added, so a thread waits for one
+// memory round trip per eight splits, not one per split.
 __global__ __launch_bounds__(256) void skinny_dx_sum(const v4i *__restrict__ part, Out o, int64_t M, int64_t K,
                                                      int32_t S) {
   const int64_t n4 = M * K / 4, kq = K / 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    v4i t = part[i];
-    for (int32_t s = 1; s < S; ++s) t += part[(int64_t)s * n4 + i];
+    v4i t = v4i{0, 0, 0, 0};
+    for (int32_t s0 = 0; s0 < S; s0 += 8) {
+      v4i p[8];
+      // unconditional loads (past S: the last split again, added as 0), so
+      // no branch separates them
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = part[(int64_t)(s0 + u < S ? s0 + u : S - 1) * n4 + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += s0 + u < S ? p[u] : v4i{0, 0, 0, 0};
+    }
     const int64_t row = i / kq, col = 4 * (i % kq);
     const float rsc = row_scale(o, row);
     if (o.vec) {
