@@ -161,15 +161,18 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
     HBM (past the 256 MB memory-side cache), as a pass over many layers
     would.  Bytes: packed weights, the int8 rows, the int32 output.  dX runs
     with a workspace (the contraction split across workgroups where that
-    applies, two kernels per call); the one-pass call is timed beside it."""
+    applies, two kernels per call); the one-pass call is timed beside it.
+    `graph_us` replays the same `steps` calls from one captured HIP graph:
+    the device-bound time per call, where the eager loop is bound by the
+    host's launch rate (the smallest shape)."""
     out = {}
     dev = torch.device("cuda:0")
 
     def timed(call, Xd, Ws, O, copies):
         first = torch.empty_like(O)
-        call(Xd, Ws[0], first)
+        call(Xd, Ws[0], first, stream)
         for i in range(3):
-            call(Xd, Ws[i % copies], O)
+            call(Xd, Ws[i % copies], O, stream)
         torch.cuda.synchronize()
         if not torch.equal(first, O):
             raise RuntimeError(f"skinny {op}: copies of the same weights gave different results")
@@ -177,32 +180,59 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for i in range(steps):
-            call(Xd, Ws[(i + 3) % copies], O)
+            call(Xd, Ws[(i + 3) % copies], O, stream)
         ev1.record(stream)
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps / 1e3, first
+
+    def graph_timed(call, Xd, Ws, O, copies, first):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                call(Xd, Ws[(i + 3) % copies], O, side)
+        O.zero_()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(first, O):
+            raise RuntimeError(f"skinny {op}: the graph replay differs from the eager calls")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            g.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        if not torch.equal(first, O):
+            raise RuntimeError(f"skinny {op}: the second graph replay differs from the eager calls")
+        del g
+        return ev0.elapsed_time(ev1) / steps / 1e3
 
     for (M, N, K) in SKINNY:
         one_pass = None
         if op == "fwd":
             X, Wp = synth.fwd_inputs(seed, M, N, K, 3)
-            call = lambda Xd, W, O: B.ternary_gemm_s8(Xd, W, C=O, stream=stream)
+            call = lambda Xd, W, O, s: B.ternary_gemm_s8(Xd, W, C=O, stream=s)
             shape, byts = (M, N), N * (K // 4) + M * K + 4 * M * N
         else:
             X, Wp = synth.dx_inputs(seed, M, N, K, 3)
             nws = B.ternary_gemm_dx_workspace(M, N, K)
             ws = torch.empty(nws, dtype=torch.uint8, device=dev)   # empty: no query per call
-            call = lambda Xd, W, O: B.ternary_gemm_s8_dx_ws(Xd, W, K, workspace=ws, dX=O, stream=stream)
-            one_pass = lambda Xd, W, O: B.ternary_gemm_s8_dx(Xd, W, K, dX=O, stream=stream)
+            call = lambda Xd, W, O, s: B.ternary_gemm_s8_dx_ws(Xd, W, K, workspace=ws, dX=O, stream=s)
+            one_pass = lambda Xd, W, O, s: B.ternary_gemm_s8_dx(Xd, W, K, dX=O, stream=s)
             shape, byts = (M, K), N * (K // 4) + M * N + 4 * M * K
         copies = max(2, -(-(512 << 20) // (N * K // 4)))
         Xd = torch.from_numpy(X).to(dev)
         Ws = torch.from_numpy(Wp).to(dev).unsqueeze(0).repeat(copies, 1, 1)
         O = torch.empty(shape, dtype=torch.int32, device=dev)
         t, first = timed(call, Xd, Ws, O, copies)
+        tg = graph_timed(call, Xd, Ws, O, copies, first)
         ops = 2 * M * N * K
         row = {"avg_us": t * 1e6, "gbps": byts / t / 1e9, "hbm_frac": byts / t / PEAK_HBM_BPS,
-               "tops": ops / t / 1e12, "algorithmic_bytes": byts, "ops": ops, "weight_copies": copies}
+               "tops": ops / t / 1e12, "algorithmic_bytes": byts, "ops": ops, "weight_copies": copies,
+               "graph_us": tg * 1e6}
         if one_pass is not None:
             t1, first1 = timed(one_pass, Xd, Ws, O, copies)
             if not torch.equal(first, first1):
