@@ -251,6 +251,57 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
     return out
 
 
+def backward_rows(B, synth, torch, stream, seed, steps):
+    """dX and dW of the pages' backward batch (1782 rows, N = 3456, K = 1280),
+    warm inputs, each over `steps` launches, eagerly and replayed from one
+    captured HIP graph (checked against the eager result).  Ops 2 MNK;
+    bytes as the step's."""
+    dev = torch.device("cuda:0")
+    M, N, K = 1782, 3456, 1280
+    A, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+    dC = synth.uniform_int8(seed, synth.STREAM_DC, M, N)
+    Ad, Wd, dCd = (torch.from_numpy(x).to(dev) for x in (A, Wp, dC))
+    cases = {"dx": (lambda O, s: B.ternary_gemm_s8_dx(dCd, Wd, K, dX=O, stream=s), (M, K)),
+             "dw": (lambda O, s: B.ternary_gemm_s8_dw(Ad, dCd, dW=O, stream=s), (K, N))}
+    out = {"workload": f"{M}x{N}x{K}"}
+    for name, (call, shape) in cases.items():
+        O = torch.empty(shape, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            call(O, stream)
+        torch.cuda.synchronize()
+        first = O.clone()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            call(O, stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t = ev0.elapsed_time(ev1) / steps / 1e3
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(steps):
+                call(O, side)
+        O.zero_()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            g.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        if not torch.equal(O, first):
+            raise RuntimeError(f"backward {name}: the graph replay differs from the eager calls")
+        tg = ev0.elapsed_time(ev1) / steps / 1e3
+        del g
+        ops = 2 * M * N * K
+        byts = kernel_work(name, M, N, K)[1]
+        out[name] = {"avg_us": t * 1e6, "graph_us": tg * 1e6, "tops": ops / tg / 1e12,
+                     "mfma_frac": ops / tg / PEAK_INT8_OPS, "gbps": byts / tg / 1e9,
+                     "kernel": int(B.plan(name, M, N, K).kernel)}
+    return out
+
+
 def prep_steps(B, synth, torch, stream, seed, steps):
     """The steps before the product, each timed over `steps` launches on
     inputs cycled through enough copies (more than 256 MB in all) that every
@@ -322,6 +373,9 @@ def main():
     ap.add_argument("--skinny-steps", type=int, default=50,
                     help="after the timed step, time the few-row forward and dX (27 and 1 rows, "
                          "cold weights) over this many launches each (0: skip)")
+    ap.add_argument("--backward-steps", type=int, default=50,
+                    help="after the timed step, time dX and dW at the pages' backward batch "
+                         "(1782 x 3456 x 1280) over this many launches each (0: skip)")
     ap.add_argument("--prep-steps", type=int, default=50,
                     help="after the timed step, time the packer and the quantizers over this many "
                          "launches each (0: skip)")
@@ -456,6 +510,8 @@ def main():
     if args.skinny_steps > 0 and not args.only:
         line["skinny_forward"] = skinny_rows(B, synth, torch, stream, args.seed, args.skinny_steps, "fwd")
         line["skinny_dx"] = skinny_rows(B, synth, torch, stream, args.seed, args.skinny_steps, "dx")
+    if args.backward_steps > 0 and not args.only:
+        line["backward_1782"] = backward_rows(B, synth, torch, stream, args.seed, args.backward_steps)
     if args.prep_steps > 0 and not args.only:
         line["prep"] = prep_steps(B, synth, torch, stream, args.seed, args.prep_steps)
     if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:

@@ -248,8 +248,9 @@ const char *ternary_gemm_status_str(int status);
  * dimensions (pointer checks excepted).
  */
 #define TGEMM_KERNEL_TILED 0   /* one 4-wave workgroup per output tile          */
-#define TGEMM_KERNEL_SPLIT 2   /* dW: the tile's contraction split between two
-                                  4-wave halves of one workgroup              */
+#define TGEMM_KERNEL_SPLIT 2   /* dW, and dX with at most 256 tiles, on 128 x 144
+                                  tiles: the tile's contraction split between
+                                  two 4-wave halves of one workgroup          */
 #define TGEMM_KERNEL_STREAM 3  /* forward (K % 64 == 0) and dX (N % 64 == 0,
                                   K % 16 == 0) on 16-byte aligned A or dC and
                                   4-byte aligned Wpacked, 32-bit offsets, at

@@ -985,20 +985,22 @@ uintptr_t align_of(const void *p) {
 }
 
 // ---------------------------------------------------------------------------
-// dW with the contraction split inside the workgroup.  dW's output is small
-// (K x N) and its contraction long (M), so at the large shapes there are only
-// about as many tiles as CUs: one 4-wave workgroup per CU leaves each SIMD a
-// single wave, whose MFMAs stop at every barrier and LDS wait.  Here a
-// workgroup has two 4-wave halves on the same tile: half h takes the
-// contraction steps j = 2t + h, each half with its own LDS stages, so every
-// SIMD runs two waves.  At the end half 1 hands its int32 sums to half 0
-// through LDS and half 0 adds and stores them: a fixed order, so the result
-// is exact and identical on every call, with no atomics and no scratch memory.
+// The contraction split inside the workgroup (dW, and dX with few tiles).
+// dW's output is small (K x N) and its contraction long (M), so at the large
+// shapes there are only about as many tiles as CUs; dX of a few thousand rows
+// (the pages' backward batch of 1782) has fewer.  One 4-wave workgroup per CU
+// then leaves each SIMD a single wave, whose MFMAs stop at every barrier and
+// LDS wait.  Here a workgroup has two 4-wave halves on the same tile: half h
+// takes the contraction steps j = 2t + h, each half with its own LDS stages,
+// so every SIMD runs two waves.  At the end half 1 hands its int32 sums to
+// half 0 through LDS and half 0 adds and stores them: a fixed order, so the
+// result is exact and identical on every call, with no atomics and no
+// scratch memory.
 // ---------------------------------------------------------------------------
-template <class T, bool FAST>
+template <int OP, class T, bool FAST>
 __global__ __attribute__((amdgpu_flat_work_group_size(2 * kThreads, 2 * kThreads), amdgpu_waves_per_eu(2)))
-void tgemm_dw_split(Args a) {
-  typedef StageBytes<DW, T> SB;
+void tgemm_split(Args a) {
+  typedef StageBytes<OP, T> SB;
   constexpr int kHalf = 2 * (SB::Q + SB::P);                      // a half's two stages
   constexpr int kRed = T::FM * T::FN * kThreads * 16;             // half 1's sums
   constexpr int kBytes = 2 * kHalf > kRed ? 2 * kHalf : kRed;
@@ -1023,11 +1025,11 @@ void tgemm_dw_split(Args a) {
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  typedef Stages<DW, T, FAST> S;
+  typedef Stages<OP, T, FAST> S;
   S st;
   st.init(a, q0, p0, tid);
   typename S::Slot slot[T::PF];
-  Frags<DW, T> fr;
+  Frags<OP, T> fr;
   fr.init(lane, wm, wn);
 
   const int32_t nk = (int32_t)((a.L + BK - 1) / BK);
@@ -2086,7 +2088,8 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 
 // Kernel per product, tile and load path:
 //   tiled  tgemm_kernel: every case but the next
-//   split  tgemm_dw_split: dW, 128 x 144 tile, contraction of 8 steps or more
+//   split  tgemm_split: dW, and dX with at most 256 tiles, on the 128 x 144
+//          tile with a contraction of 8 steps or more
 //   stream tgemm_stream: large forward and dX outputs (stream_plan)
 //   skinny tgemm_skinny: forward with at most 32 rows (skinny_plan)
 // (A variant that loads the int8 operand of the forward and dX straight into
@@ -2206,16 +2209,21 @@ void launch_skinny(const KArgs &ka, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_skinny<MF, NB, AL>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
 }
 
-int pick_kernel(int op, int tile, int64_t L) {
+// the contraction split between two halves of a workgroup: dW on the
+// 128 x 144 tile, and dX on that tile when its tiles do not fill the CUs;
+// at least 8 steps
+int pick_kernel(int op, int tile, int64_t L, int64_t tiles) {
   if (op == DW && tile == TW && L >= 8 * BK) return KSPLIT;
+  if (op == DX && tile == TW && L >= 8 * BK && tiles <= 256) return KSPLIT;
   return KTILED;
 }
 
 template <int OP>
 int lds_of_kernel(int kernel, int tile) {
   if (kernel == KSPLIT) {
-    typedef StageBytes<DW, Tiles<DW>::W> SB;
-    const int stages = 4 * (SB::Q + SB::P), red = Tiles<DW>::W::FM * Tiles<DW>::W::FN * kThreads * 16;
+    typedef typename Tiles<OP>::W T;
+    typedef StageBytes<OP, T> SB;
+    const int stages = 4 * (SB::Q + SB::P), red = T::FM * T::FN * kThreads * 16;
     return stages > red ? stages : red;
   }
   return lds_of_tile<OP>(tile);
@@ -2229,13 +2237,13 @@ int kernel_lds(int op, int kernel, int tile) {
 
 template <int OP>
 hipError_t launch_op(const Args &a, int kernel, int tile, bool fast, hipStream_t stream) {
-  if constexpr (OP == DW) {
+  if constexpr (OP == DW || OP == DX) {
     if (kernel == KSPLIT) {
-      typedef typename Tiles<DW>::W T;
+      typedef typename Tiles<OP>::W T;
       if (fast)
-        hipLaunchKernelGGL((tgemm_dw_split<T, true>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
+        hipLaunchKernelGGL((tgemm_split<OP, T, true>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
       else
-        hipLaunchKernelGGL((tgemm_dw_split<T, false>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
+        hipLaunchKernelGGL((tgemm_split<OP, T, false>), dim3(a.tiles), dim3(2 * kThreads), 0, stream, a);
       return hipGetLastError();
     }
   }
@@ -2387,7 +2395,7 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
 
-  const int kernel = pick_kernel(op, tile, s.L);
+  const int kernel = pick_kernel(op, tile, s.L, a.tiles);
   hipError_t e;
   if (op == FWD)
     e = launch_op<FWD>(a, kernel, tile, fast, stream);
@@ -2535,7 +2543,7 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->workgroups = plan->tiles;
   plan->tiles_per_workgroup = 1;
   plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
-  plan->kernel = pick_kernel(op, tile, s.L);
+  plan->kernel = pick_kernel(op, tile, s.L, plan->tiles);
   plan->threads_per_workgroup = plan->kernel == KSPLIT ? 2 * kThreads : kThreads;
   plan->lds_bytes = kernel_lds(op, plan->kernel, tile);
   return TGEMM_OK;

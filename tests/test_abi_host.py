@@ -118,7 +118,7 @@ def _coverage(op, M, N, K):
 @pytest.mark.parametrize("op,M,N,K", [
     ("fwd", 1, 16, 16), ("fwd", 300, 272, 96), ("fwd", 16384, 3456, 1280),
     ("fwd", 2048, 2048, 65536), ("fwd", 8191, 4001, 1040), ("fwd", 77, 4099, 32),
-    ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280),
+    ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280), ("dx", 1782, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
     + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES]
     + [("fwd",) + s for s in SKINNY_SHAPES] + [("dx",) + s for s in SKINNY_DX_SHAPES])
@@ -142,7 +142,8 @@ def test_parity_shapes_reach_every_tile_and_path():
     # and every kernel on each load path it serves
     kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1),
                        (B.KERNEL_SKINNY, 1)},
-               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1), (B.KERNEL_SKINNY, 1)},
+               "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1), (B.KERNEL_SKINNY, 1),
+                      (B.KERNEL_SPLIT, 0), (B.KERNEL_SPLIT, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
     for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES),
@@ -167,7 +168,12 @@ def test_kernel_choice():
     assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
     assert B.plan("dx", 16384, 3456, 1288).kernel == B.KERNEL_TILED    # K % 16 != 0
     assert B.plan("dx", 16384, 3400, 1280).kernel == B.KERNEL_TILED    # N % 64 != 0
-    assert B.plan("dx", 1782, 3456, 1280).kernel == B.KERNEL_TILED     # 32 tiles of 512 x 160
+    # 32 tiles of 512 x 160 are too few for the stream kernel; 126 of 128 x 144
+    # take the contraction split between two halves of a workgroup
+    pl = B.plan("dx", 1782, 3456, 1280)
+    assert (pl.kernel, pl.tile_rows, pl.tile_cols, pl.threads_per_workgroup) == (B.KERNEL_SPLIT, 128, 144, 512)
+    assert B.plan("dx", 4100, 80, 3904).kernel == B.KERNEL_TILED     # 924 tiles fill the CUs
+    assert B.plan("dx", 4100, 80, 912).kernel == B.KERNEL_TILED      # 2 steps
     for s in DX_STREAM_SHAPES:
         assert B.plan("dx", *s).kernel == B.KERNEL_STREAM, s
     assert B.plan("dw", 16384, 3456, 1280).kernel == B.KERNEL_SPLIT
@@ -183,7 +189,7 @@ def test_kernel_choice():
     for s in SKINNY_DX_SHAPES:
         assert B.plan("dx", *s).kernel == B.KERNEL_SKINNY, s
     assert B.plan("dx", 27, 16384 + 32, 16384).kernel == B.KERNEL_TILED   # N % 64 != 0
-    assert B.plan("dx", 27, 16384, 16392).kernel == B.KERNEL_TILED        # K % 16 != 0
+    assert B.plan("dx", 27, 16384, 16392).kernel == B.KERNEL_SPLIT        # K % 16 != 0: not skinny
     assert B.plan("dx", 33, 16384, 16384).kernel != B.KERNEL_SKINNY       # more than 32 rows
     assert B.plan("dx", 27, 16384, 16384, align=8).kernel == B.KERNEL_TILED
     assert B.plan("dw", 27, 16384, 16384).kernel != B.KERNEL_SKINNY

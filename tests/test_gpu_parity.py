@@ -329,6 +329,7 @@ SCALED_CASES = [
     ("dx", 300, 96, 272),         # tiled dX
     ("dx", 27, 3456, 1280),       # skinny dX, the pages' 27 rows
     ("dx", 5, 8192, 8192),        # skinny dX, 64-column blocks, one 16-row block
+    ("dx", 1782, 3456, 1280),     # dX, contraction split between two halves of a workgroup
     ("dw", 1090, 912, 4112),      # split dW kernel
     ("dw", 97, 271, 299),         # tiled dW, ragged
     ("dw", 16384, 3456, 1280),    # the timed shape
