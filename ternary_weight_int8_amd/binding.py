@@ -237,6 +237,8 @@ def _workspace(workspace, M, N, K, dC, Wpacked, stream):
         if stream is not None:
             workspace.record_stream(stream)   # freed here, in use on `stream`
     _check(workspace, torch.uint8, workspace.dim(), "workspace")
+    if workspace.device != dC.device:
+        raise ValueError(f"workspace must be on {dC.device}, got {workspace.device}")
     if workspace.numel() == 0:
         return None, 0, workspace
     return workspace.data_ptr(), workspace.numel(), workspace
