@@ -156,7 +156,7 @@ int ternary_gemm_s8_dx_scaled(const int8_t *dC, const uint8_t *Wpacked, const fl
  * blocks are too few to fill the chip, the contraction is split across
  * workgroups: each writes its int32 partial sums to the workspace and a
  * second kernel adds them in split order, which is faster when each W row is
- * long (27 x 16384 x 16384: 33 against 49 us).  The workspace must then hold
+ * long (27 x 16384 x 16384: about 32 against 46 us).  The workspace must then hold
  * ternary_gemm_dx_workspace() bytes and be 16-byte aligned; a NULL, smaller
  * or unaligned workspace runs the one-pass kernels instead, with the same
  * results.  The workspace's contents on entry do not matter and are garbage
