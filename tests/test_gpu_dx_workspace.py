@@ -137,3 +137,23 @@ def test_split_dx_misaligned_output(kind):
     b = host(buf)
     assert b[0] == -7 and b[-1] == -7
     assert_exact(b[1:1 + M * K].reshape(M, K), want, f"dx workspace misaligned {kind}")
+
+
+def test_concurrent_calls_with_their_own_workspaces():
+    # two streams, each with its own workspace, run the split dX at the same
+    # time on different shapes; both results match the oracle
+    shapes = [(27, 16384, 16384), (16, 4096, 8192)]
+    say("dx workspace on two streams")
+    ins = [_inputs(M, N, K, 3) for (M, N, K) in shapes]
+    devs = [(dev(dC), dev(Wp)) for (dC, Wp) in ins]
+    wss = [torch.empty(B.ternary_gemm_dx_workspace(*s), dtype=torch.uint8, device=DEV) for s in shapes]
+    outs = [torch.empty((M, K), dtype=torch.int32, device=DEV) for (M, N, K) in shapes]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    want = [oracle.dx(dC, Wp, K) for (dC, Wp), (M, N, K) in zip(ins, shapes)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (M, N, K) in enumerate(shapes):
+            B.ternary_gemm_s8_dx_ws(devs[i][0], devs[i][1], K, workspace=wss[i], dX=outs[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i, (M, N, K) in enumerate(shapes):
+            assert_exact(host(outs[i]), want[i], f"stream {i} rep {rep} {M}x{N}x{K}")
