@@ -740,12 +740,24 @@ __device__ __forceinline__ void store_tile(const Args &a, const v4i (&acc)[T::FM
   const int64_t rbase = r0 + (lane & 15);
   const int64_t cbase = c0 + (lane >> 4) * 4;
   if (a.o.vec && inside) {
+    // Lane l of a fragment holds row l % 16, so neighbouring lanes would hit
+    // different rows, which a CU drains at a third of the rate of
+    // row-contiguous stores.  A lane permutation (ds_bpermute, no LDS memory;
+    // every lane is active here) moves row L / 4, columns 4 (L % 4) .. + 3 to
+    // lane L, so four neighbouring lanes write one 16-column run of a row.
+    const int src = 4 * ((lane >> 2) + 16 * (lane & 3));
+    const int64_t rp = r0 + (lane >> 2), cp = c0 + 4 * (lane & 3);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-      const int64_t row = rbase + i * 16;
+      const int64_t row = rp + i * 16;
       const float r = row_scale(a.o, row);
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) put4(a.o, a.Cc, row, cbase + j * 16, acc[i][j], r);
+      for (int j = 0; j < T::FN; ++j) {
+        v4i v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_ds_bpermute(src, acc[i][j][e]);
+        put4(a.o, a.Cc, row, cp + j * 16, v, r);
+      }
     }
     return;
   }
