@@ -407,3 +407,82 @@ def test_scaled_output_misaligned(op, M, N, K):
     assert b[0] == -7 and b[-1] == -7
     assert_exact(b[1:1 + R * C].reshape(R, C), oracle.scale_output(acc, rs, cs, "bf16").view(np.int16),
                  f"scaled misaligned {op}")
+
+
+# ---------------------------------------------------------------------------
+# the scaled outputs' reading, pinned on the GPU: acc values and scales chosen
+# so that RN(RN(acc * rs) * cs) differs from RN(acc * RN(rs * cs)) are placed
+# in chosen output elements of every kernel path; those elements must equal
+# the exact binary32 model (tests/exact_f32.py) and every element the oracle
+# ---------------------------------------------------------------------------
+
+READING_SHAPES = [("fwd", 16, 100, 64), ("fwd", 300, 272, 96), ("fwd", 4096, 4608, 64),
+                  ("dx", 27, 3456, 1280), ("dx", 300, 96, 272), ("dx", 16300, 3456, 1296),
+                  ("dw", 97, 271, 299), ("dw", 1090, 912, 4112)]
+
+
+def _reading_case(op, M, N, K):
+    """Inputs whose exact product holds case i's acc at output (i, 0) (forward,
+    dX) or (i, i) (dW), with random values everywhere else."""
+    from test_oracle import SCALE_ORDER_CASES
+    accs = [c[0] for c in SCALE_ORDER_CASES]
+    seed = 7 + M + N + K
+    if op == "fwd":
+        A, Wp = synth.fwd_inputs(seed, M, N, K, 3)
+        Wp[0, :] = 0
+        Wp[0, 0] = 0x01                 # column 0: weight +1 at k = 0 only
+        for i, v in enumerate(accs):
+            A[i, 0] = v
+        return (A, Wp), [(i, 0) for i in range(len(accs))]
+    if op == "dx":
+        dC, Wp = synth.dx_inputs(seed, M, N, K, 3)
+        Wp[:, 0] &= 0xFC                # weight 0 at k = 0 in every row n ...
+        Wp[0, 0] |= 0x01                # ... but +1 in row n = 0
+        for i, v in enumerate(accs):
+            dC[i, 0] = v
+        return (dC, Wp), [(i, 0) for i in range(len(accs))]
+    A, dC = synth.dw_inputs(seed, M, N, K)
+    for i, v in enumerate(accs):
+        A[:, i] = 0
+        A[0, i] = 1                     # column i of A picks row 0 of dC
+        dC[0, i] = v
+    return (A, dC), [(i, i) for i in range(len(accs))]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("op,M,N,K", READING_SHAPES)
+def test_scaled_reading_exact_cases(op, M, N, K, kind):
+    import exact_f32 as X
+    from test_oracle import SCALE_ORDER_CASES
+    torch = _torch_mod()
+    say(f"scaled reading {kind} {op} {M}x{N}x{K} plan={tile_of(op, M, N, K)}")
+    ins, spots = _reading_case(op, M, N, K)
+    acc = oracle.fwd(*ins) if op == "fwd" else oracle.dx(ins[0], ins[1], K) if op == "dx" else oracle.dw(*ins)
+    R, C = acc.shape
+    dtype = torch.float32 if kind == "f32" else torch.bfloat16
+    # the forward and dX take one column scale for the whole output: one call
+    # per case; dW takes a scale per column: one call holds every case
+    calls = [[i] for i in range(len(spots))] if op != "dw" else [list(range(len(spots)))]
+    for cases in calls:
+        rs = synth.positive_scales(R, synth.STREAM_ROW_SCALE, R)
+        cs = synth.positive_scales(C, synth.STREAM_COL_SCALE, C) if op == "dw" else None
+        for i in cases:
+            acc_i, rb, cb = SCALE_ORDER_CASES[i]
+            r, c = spots[i]
+            assert int(acc[r, c]) == acc_i
+            rs[r] = X.f32_of_bits(rb)
+            if op == "dw":
+                cs[c] = X.f32_of_bits(cb)
+            else:
+                cs = X.f32_of_bits(cb)
+        got = _bits(_gpu_scaled(op, ins, K, rs, cs, dtype))
+        want = oracle.scale_output(acc, rs, cs, kind)
+        assert_exact(got, want.view(np.int32) if kind == "f32" else want.view(np.int16),
+                     f"scaled reading {kind} {op} {M}x{N}x{K}")
+        for i in cases:
+            acc_i, rb, cb = SCALE_ORDER_CASES[i]
+            r, c = spots[i]
+            y = X.rn32(X.rn32(acc_i * X.exact(X.f32_of_bits(rb))) * X.exact(X.f32_of_bits(cb)))
+            wb = X.bits32(y) if kind == "f32" else X.bits_bf16(X.rn_bf16(y))
+            gb = int(got[r, c]) & (0xFFFFFFFF if kind == "f32" else 0xFFFF)
+            assert gb == wb, (op, i, hex(gb), hex(wb))

@@ -219,3 +219,38 @@ def test_quantize_cols_grid_stride():
     q, s = oracle.quantize(X, "bf16", "cols")
     assert_same(host(S).view(np.uint32), s.view(np.uint32), "column scales grid-stride")
     assert_same(host(Q), q, "cols grid-stride")
+
+
+@pytest.mark.parametrize("kind_path", ["elements", "vector"])
+def test_quantize_exact_reading_cases(kind_path):
+    # values chosen so that the division readings (s = RN(max / 127), q =
+    # rint(RN(x / s))) differ from the reciprocal ones; scales and values must
+    # equal the exact binary32 model (tests/exact_f32.py) and the oracle, on
+    # rows and on columns
+    from fractions import Fraction
+
+    import exact_f32 as X
+    from test_oracle import SCALE_DIVISION_CASES, VALUE_DIVISION_CASES
+    say(f"quantize exact reading cases ({kind_path})")
+    C = 3 if kind_path == "elements" else 64
+    rows = []
+    for mb in SCALE_DIVISION_CASES:
+        m = X.f32_of_bits(mb)
+        rows.append([m, -m / np.float32(3), np.float32(0.25)])
+    for mb, xb in VALUE_DIVISION_CASES:
+        rows.append([X.f32_of_bits(mb), X.f32_of_bits(xb), -X.f32_of_bits(xb)])
+    x = np.zeros((len(rows), C), dtype=np.float32)
+    x[:, :3] = np.array(rows, dtype=np.float32)
+    for axis, xin in (("rows", x), ("cols", np.ascontiguousarray(x.T))):
+        fn = B.ternary_quantize_rows if axis == "rows" else B.ternary_quantize_cols
+        Q, S = fn(dev(xin))
+        q, s = oracle.quantize(xin, "f32", axis)
+        got_q, got_s = host(Q), host(S).view(np.uint32)
+        assert_same(got_s, s.view(np.uint32), f"{axis} scales")
+        assert_same(got_q, q, f"{axis} values")
+        gq = got_q if axis == "rows" else got_q.T
+        for r, vals in enumerate(rows):
+            sr = X.rn32(max(abs(X.exact(v)) for v in vals) / 127)
+            assert int(got_s[r]) == X.bits32(sr), (axis, r)
+            want = [max(-127, min(127, X.round_half_even(X.rn32(X.exact(v) / sr)))) for v in vals]
+            assert gq[r, :3].tolist() == want, (axis, r)

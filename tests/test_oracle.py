@@ -6,9 +6,12 @@ products, closed forms, exact extremes at the int32 bound, and numpy's int64
 matmul (a library routine) over a decode written separately from the page's
 byte table.  Each group below names the mistake it is there to catch.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
+import exact_f32 as X
 import oracle
 from golden_io import read_kv
 from ternary_weight_int8_amd import synth
@@ -374,6 +377,106 @@ def test_scaled_orientation_exact_case():
     big = np.array([[2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 31)]], dtype=np.int32)
     got = oracle.scale_output(big, np.ones(1, np.float32), np.float32(1.0), "f32")
     np.testing.assert_array_equal(got, np.array([[2.0 ** 24, 2.0 ** 24 + 4, -2.0 ** 31]], np.float32))
+
+
+# Exact-value pins of the two floating-point readings.  Expected values come
+# from tests/exact_f32.py, an exact rational model of binary32 round-to-
+# nearest-even, not from numpy's float32 arithmetic.  Each case was chosen
+# (by a search with that model) so that the reading taken and a plausible
+# alternative give different bits: a mistake in the order or kind of the
+# steps fails here, where the error-bound pins above cannot tell.
+#   scaled output:  RN(RN(acc * rs) * cs)      not  RN(acc * RN(rs * cs))
+#   quantizer:      s = RN(max / 127)          not  RN(max * RN(1 / 127))
+#                   q = rint(RN(x / s))        not  rint(RN(x * RN(1 / s)))
+# ---------------------------------------------------------------------------
+
+SCALE_ORDER_CASES = [(-124, 0x3DC059A7, 0x3D1C650C), (107, 0x3DC3078A, 0x3DBDC37C),
+                     (85, 0x3DAB91B9, 0x3D641AF9)]          # (acc, row scale bits, column scale bits)
+SCALE_DIVISION_CASES = [0x428E86F4, 0x424B1A5C, 0x429BE8FB]   # max |x| bits
+VALUE_DIVISION_CASES = [(0x42C4A784, 0x419DF160), (0x42681D30, 0x419062C9),
+                        (0x42B818E2, 0x412826DB), (0x429CF288, 0x4250D9EC)]   # (max |x| bits, x bits)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def test_exact_model_matches_ieee_on_hand_values():
+    # the model itself, on values whose binary32 rounding is known by hand
+    R = X.rn32
+    assert R(Fraction(1, 3)) == Fraction(11184811, 2 ** 25)          # 0x3EAAAAAB
+    assert R(Fraction(1) + Fraction(1, 2 ** 24)) == 1                   # tie -> even (1.0)
+    assert R(Fraction(1) + Fraction(3, 2 ** 24)) == 1 + Fraction(2, 2 ** 23)   # tie -> even (up)
+    assert R(Fraction(2 ** 24 + 1)) == 2 ** 24 and R(Fraction(2 ** 24 + 3)) == 2 ** 24 + 4
+    assert R(Fraction(3, 2 ** 150)) == Fraction(2, 2 ** 149)             # subnormal tie -> even
+    assert X.bits32(R(Fraction(1, 127))) == 0x3C010204
+
+
+def test_scaled_output_order_exact_cases():
+    for acc, rb, cb in SCALE_ORDER_CASES:
+        rs, cs = X.f32_of_bits(rb), X.f32_of_bits(cb)
+        want = X.rn32(X.rn32(acc * X.exact(rs)) * X.exact(cs))
+        other = X.rn32(acc * X.rn32(X.exact(rs) * X.exact(cs)))
+        assert want != other, "the case must separate the two orders"
+        a = np.array([[acc]], dtype=np.int32)
+        got = oracle.scale_output(a, np.array([rs]), np.array([cs]), "f32")
+        assert int(_bits(got)[0, 0]) == X.bits32(want), (acc, hex(rb), hex(cb))
+        got_s = oracle.scale_output(a, np.array([rs]), cs, "f32")       # one scale for every column
+        assert int(_bits(got_s)[0, 0]) == X.bits32(want)
+
+
+def test_scaled_output_every_element_exact():
+    # every element of a random case against the exact model, acc up to 2^30
+    # (so the int32 -> float conversion rounds too)
+    R, C = 12, 10
+    acc = ((synth.splitmix64(21, 9, R * C) >> np.uint64(33)).astype(np.int64) - (1 << 30)).astype(np.int32)
+    acc = acc.reshape(R, C)
+    rs = synth.positive_scales(21, synth.STREAM_ROW_SCALE, R)
+    cs = synth.positive_scales(21, synth.STREAM_COL_SCALE, C)
+    got = _bits(oracle.scale_output(acc, rs, cs, "f32"))
+    for r in range(R):
+        for c in range(C):
+            y = X.rn32(X.rn32(X.rn32(Fraction(int(acc[r, c]))) * X.exact(rs[r])) * X.exact(cs[c]))
+            assert int(got[r, c]) == X.bits32(y), (r, c)
+
+
+def test_quantize_scale_is_a_division_exact_cases():
+    inv127 = X.rn32(Fraction(1, 127))
+    for mb in SCALE_DIVISION_CASES:
+        m = X.f32_of_bits(mb)
+        s = X.rn32(X.exact(m) / 127)
+        assert s != X.rn32(X.exact(m) * inv127), "the case must separate the two readings"
+        x = np.array([[m, -m / np.float32(3), np.float32(0.25)]], dtype=np.float32)
+        for axis, xin in (("rows", x), ("cols", np.ascontiguousarray(x.T))):
+            _, sc = oracle.quantize(xin, "f32", axis)
+            assert int(_bits(sc)[0]) == X.bits32(s), (axis, hex(mb))
+
+
+def test_quantize_value_is_a_division_exact_cases():
+    for mb, xb in VALUE_DIVISION_CASES:
+        m, x = X.f32_of_bits(mb), X.f32_of_bits(xb)
+        s = X.rn32(X.exact(m) / 127)
+        q = X.round_half_even(X.rn32(X.exact(x) / s))
+        other = X.round_half_even(X.rn32(X.exact(x) * X.rn32(1 / s)))
+        assert q != other, "the case must separate the two readings"
+        row = np.array([[m, x, -x]], dtype=np.float32)
+        for axis, xin in (("rows", row), ("cols", np.ascontiguousarray(row.T))):
+            qv, _ = oracle.quantize(xin, "f32", axis)
+            qv = qv.reshape(-1)
+            assert qv.tolist() == [127, q, -q], (axis, hex(mb), hex(xb))
+
+
+def test_quantize_every_element_exact():
+    # every element of random rows against the exact model of the rule
+    x = synth.float_inputs(22, synth.STREAM_X, 6, 40, "f32")
+    q, s = oracle.quantize(x, "f32", "rows")
+    for r in range(x.shape[0]):
+        m = max(abs(X.exact(v)) for v in x[r])
+        sr = X.rn32(m / 127)
+        assert int(_bits(s)[r]) == X.bits32(sr)
+        for c in range(x.shape[1]):
+            qq = max(-127, min(127, X.round_half_even(X.rn32(X.exact(x[r, c]) / sr))))
+            assert int(q[r, c]) == qq, (r, c)
 
 
 # ---------------------------------------------------------------------------
