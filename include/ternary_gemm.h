@@ -258,6 +258,12 @@ const char *ternary_gemm_status_str(int status);
                                   512 x 160 (dX): one persistent 8-wave
                                   workgroup per CU, operands loaded straight
                                   into LDS                                    */
+#define TGEMM_KERNEL_DBUF 5    /* forward, int32 output, K % 256 == 0, K >= 1024,
+                                  16-byte aligned A, 4-byte aligned Wpacked
+                                  and C, 32-bit offsets, at least four
+                                  256 x 96 tiles per CU: one persistent 4-wave
+                                  workgroup per CU, each wave storing its
+                                  previous tile while it computes the next  */
 #define TGEMM_KERNEL_SKINNY 4  /* forward with M <= 32, K % 64 == 0, 16-byte
                                   aligned A and Wpacked; dX with M <= 32,
                                   N % 64 == 0, K % 16 == 0, 16-byte aligned dC
@@ -277,10 +283,22 @@ typedef struct tgemm_plan {
     int32_t lds_bytes;
     int32_t fast_path;
     int32_t kernel;
+    int32_t xcds;              /* XCDs of the machine planned for            */
 } tgemm_plan;
 
 int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align,
                       tgemm_plan *plan);
+
+/*
+ * The same plan for a machine with `cus` compute units in `xcds` XCDs (cus a
+ * multiple of xcds; TGEMM_ERR_DIM otherwise).  ternary_gemm_plan plans for
+ * MI355X (256 CUs, 8 XCDs); the calls plan for the device they run on, whose
+ * counts ternary_gemm_machine reports (it queries the current HIP device
+ * once and keeps the answer; TGEMM_ERR_HIP if there is none).
+ */
+int ternary_gemm_plan_on(int op, int64_t M, int64_t N, int64_t K, int64_t align,
+                         int32_t cus, int32_t xcds, tgemm_plan *plan);
+int ternary_gemm_machine(int32_t *cus, int32_t *xcds);
 
 /*
  * Output tile that workgroup `workgroup` computes in its iteration

@@ -23,6 +23,8 @@ EXPORTS = (
     "ternary_gemm_s8_dw",
     "ternary_gemm_status_str",
     "ternary_gemm_plan",
+    "ternary_gemm_plan_on",
+    "ternary_gemm_machine",
     "ternary_gemm_tile_of",
     "ternary_gemm_s8_scaled",
     "ternary_gemm_s8_dx_scaled",
@@ -48,10 +50,11 @@ class TgemmPlan(ctypes.Structure):
         ("band_cols", ctypes.c_int32),
         ("threads_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
         ("fast_path", ctypes.c_int32), ("kernel", ctypes.c_int32),
+        ("xcds", ctypes.c_int32),
     ]
 
 
-KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM, KERNEL_SKINNY = 0, 2, 3, 4   # TgemmPlan.kernel
+KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM, KERNEL_SKINNY, KERNEL_DBUF = 0, 2, 3, 4, 5   # TgemmPlan.kernel
 
 
 class TernaryGemmError(RuntimeError):
@@ -80,6 +83,11 @@ def lib():
         L.ternary_gemm_status_str.restype = ctypes.c_char_p
         L.ternary_gemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.POINTER(TgemmPlan)]
         L.ternary_gemm_plan.restype = ctypes.c_int
+        L.ternary_gemm_plan_on.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(TgemmPlan)]
+        L.ternary_gemm_plan_on.restype = ctypes.c_int
+        L.ternary_gemm_machine.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.ternary_gemm_machine.restype = ctypes.c_int
         L.ternary_gemm_tile_of.argtypes = [ctypes.POINTER(TgemmPlan), i64, i64,
                                            ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.ternary_gemm_tile_of.restype = ctypes.c_int
@@ -130,9 +138,23 @@ def ternary_gemm_dx_workspace(M: int, N: int, K: int, align: int = 256) -> int:
     return b.value
 
 
-def plan(op: str, M: int, N: int, K: int, align: int = 256):
+def machine():
+    """(compute units, XCDs) of the current HIP device, as the calls plan for it."""
+    cus, xcds = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().ternary_gemm_machine(ctypes.byref(cus), ctypes.byref(xcds))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_machine", st, status_str(st))
+    return cus.value, xcds.value
+
+
+def plan(op: str, M: int, N: int, K: int, align: int = 256, cus: int = None, xcds: int = None):
+    """The launch plan of a call, for MI355X (256 CUs, 8 XCDs) unless cus and
+    xcds name another machine."""
     pl = TgemmPlan()
-    st = lib().ternary_gemm_plan(OPS[op], M, N, K, align, ctypes.byref(pl))
+    if cus is None and xcds is None:
+        st = lib().ternary_gemm_plan(OPS[op], M, N, K, align, ctypes.byref(pl))
+    else:
+        st = lib().ternary_gemm_plan_on(OPS[op], M, N, K, align, cus, xcds, ctypes.byref(pl))
     if st != OK:
         raise TernaryGemmError("ternary_gemm_plan", st, status_str(st))
     return pl

@@ -54,6 +54,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ternary_gemm.h"
 
 namespace {
@@ -167,11 +169,13 @@ struct Args {
   int32_t tiles_c;    // column tiles
   int32_t band_cols;  // tile columns per band of the workgroup -> tile order
   int32_t tiles;      // total tiles (= workgroups)
+  int32_t xcds;       // workgroup b runs on XCD b % xcds
 };
 
 // ---------------------------------------------------------------------------
-// Workgroup -> tile order.  The hardware hands workgroup ids to the eight
-// XCDs round-robin (id % 8), and each XCD has its own L2.  xcd_tile gives each
+// Workgroup -> tile order.  The hardware hands workgroup ids to the XCDs
+// round-robin (id % xcds; MI355X has eight), and each XCD has its own L2.
+// xcd_tile gives each
 // XCD a contiguous range of positions in a linear tile order (a bijection on
 // [0, tiles)).  That order runs row by row inside bands of band_cols tile
 // columns, band after band, so the tiles an XCD runs together share input
@@ -179,9 +183,9 @@ struct Args {
 // The host picks the band count that minimises the operand bytes the eight
 // XCDs fetch between them.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int32_t xcd_tile(int32_t wg, int32_t tiles) {
-  const int32_t q = tiles / 8, r = tiles % 8;
-  const int32_t x = wg % 8, j = wg / 8;
+__host__ __device__ inline int32_t xcd_tile(int32_t wg, int32_t tiles, int32_t xcds) {
+  const int32_t q = tiles / xcds, r = tiles % xcds;
+  const int32_t x = wg % xcds, j = wg / xcds;
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
@@ -793,8 +797,8 @@ void tgemm_kernel(Args a) {
   const int wm = wave / T::WN, wn = wave % T::WN;
 
   int32_t tr, tc;
-  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles), a.tiles / a.tiles_c, a.tiles_c, a.band_cols, &tr,
-          &tc);
+  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles, a.xcds), a.tiles / a.tiles_c, a.tiles_c, a.band_cols,
+          &tr, &tc);
   const int64_t q0 = (int64_t)tr * T::BM;
   const int64_t p0 = (int64_t)tc * T::BN;
 
@@ -916,9 +920,8 @@ Shape shape_of(int op, int64_t M, int64_t N, int64_t K) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Pick the tile with the least estimated time: rounds of one workgroup per
-// CU (256 CUs) times the MACs of one tile at that tile's efficiency.
-int pick_tile(const Shape &s) {
-  const int64_t cus = 256;
+// CU times the MACs of one tile at that tile's efficiency.
+int pick_tile(const Shape &s, int64_t cus) {
   int best = TS;
   double best_cost = 0;
   for (int t = 0; t < kTiles; ++t) {
@@ -933,17 +936,17 @@ int pick_tile(const Shape &s) {
   return best;
 }
 
-// Bands of tile columns for the workgroup order: with nb bands, each XCD
-// reads about nb/8 of the Q operand (rows) and 1/nb of the P operand
-// (columns); the eight XCDs fetch about nb*Q + 8*P/nb bytes between them.
-int32_t pick_band_cols(int op, int64_t M, int64_t N, int64_t K, int32_t tiles_c) {
+// Bands of tile columns for the workgroup order: with nb bands, each of the
+// x XCDs reads about nb/x of the Q operand (rows) and 1/nb of the P operand
+// (columns); the XCDs fetch about nb*Q + x*P/nb bytes between them.
+int32_t pick_band_cols(int op, int64_t M, int64_t N, int64_t K, int32_t tiles_c, int32_t xcds) {
   const double q = op == DX ? (double)M * N : (double)M * K;          // Q operand bytes
   const double p = op == DW ? (double)M * N : (double)N * (K / 4);    // P operand bytes
   int best_nb = 1;
   double best = 0;
-  for (int nb = 1; nb <= 8; nb *= 2) {
+  for (int nb = 1; nb <= xcds; nb *= 2) {
     if (nb > tiles_c) break;
-    const double bytes = nb * q + 8.0 * p / nb;
+    const double bytes = nb * q + (double)xcds * p / nb;
     if (nb == 1 || bytes < best) {
       best = bytes;
       best_nb = nb;
@@ -1026,8 +1029,8 @@ void tgemm_split(Args a) {
   int8_t *const sp = sq + 2 * SB::Q;
 
   int32_t tr, tc;
-  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles), a.tiles / a.tiles_c, a.tiles_c, a.band_cols, &tr,
-          &tc);
+  tile_rc(xcd_tile((int32_t)blockIdx.x, a.tiles, a.xcds), a.tiles / a.tiles_c, a.tiles_c, a.band_cols,
+          &tr, &tc);
   const int64_t q0 = (int64_t)tr * T::BM;
   const int64_t p0 = (int64_t)tc * T::BN;
 
@@ -1233,6 +1236,7 @@ struct SArgs {
   int32_t kb;         // packed row stride (K / 4)
   int32_t tiles_c, tiles;
   int32_t nk;         // L / 64
+  int32_t xcds;       // workgroup b runs on XCD b % xcds
 };
 
 // The decode of a wave's own packed dwords, in two halves so that the reads
@@ -1279,12 +1283,13 @@ void tgemm_stream(SArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Tiles of this workgroup: the tile positions (row-major over the tile
-  // grid) are split into eight contiguous runs, one per XCD (workgroup b runs
-  // on XCD b % 8), and the nx workgroups of an XCD take every nx-th position
-  // of its run, so the tiles an XCD works on at one time share Q rows and the
+  // grid) are split into one contiguous run per XCD (workgroup b runs on XCD
+  // b % xcds), and the nx workgroups of an XCD take every nx-th position of
+  // its run, so the tiles an XCD works on at one time share Q rows and the
   // weight columns in its L2.
-  const int32_t nx = (int32_t)gridDim.x / 8, xcd = (int32_t)blockIdx.x % 8, j0 = (int32_t)blockIdx.x / 8;
-  const int32_t q8 = a.tiles / 8, r8 = a.tiles % 8;
+  const int32_t nx = (int32_t)gridDim.x / a.xcds, xcd = (int32_t)blockIdx.x % a.xcds;
+  const int32_t j0 = (int32_t)blockIdx.x / a.xcds;
+  const int32_t q8 = a.tiles / a.xcds, r8 = a.tiles % a.xcds;
   const int32_t start = xcd * q8 + (xcd < r8 ? xcd : r8) + j0;
   const int32_t cnt = q8 + (xcd < r8 ? 1 : 0);
   const int32_t ntile = cnt > j0 ? (cnt - j0 + nx - 1) / nx : 0;
@@ -1615,6 +1620,7 @@ struct KArgs {
   int32_t M, N, K;
   int32_t nfull;      // whole super-steps, K / 256
   int32_t vq;         // 64-steps of the last, partial super-step (K % 256 / 64), or 0
+  int32_t xcds;       // workgroup b runs on XCD b % xcds
 };
 
 // LDS: the reduction buffer (per wave, the tile's 16 MF rows of 4 NB column
@@ -1728,7 +1734,7 @@ void tgemm_skinny(KArgs a) {
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   // column block in the XCD-contiguous order (as the skinny dX kernel)
-  const int32_t n0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x) * 16 * NB;
+  const int32_t n0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x, a.xcds) * 16 * NB;
   const int64_t kb = a.K / 4;
 
   const uint8_t *wr[NB];
@@ -1819,6 +1825,7 @@ struct XArgs {
   Out o;              // column scale, when scaled: o.cscal (o.cs is null)
   int32_t M, N, K;
   int32_t nsteps;     // N / 64
+  int32_t xcds;       // workgroup b runs on XCD b % xcds
 };
 
 template <int NB>
@@ -1879,7 +1886,7 @@ void tgemm_skinny_dx(XArgs a) {
   // contiguous run of blocks, so the blocks that share a 128-byte line of a
   // packed row read it through one L2 (in the plain order, eight XCDs each
   // fetched every line)
-  const int32_t k0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x) * 16 * NB;
+  const int32_t k0 = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x, a.xcds) * 16 * NB;
   const int64_t kb = a.K / 4;
   const uint8_t *wl = a.Wp + (int64_t)lane * kb + k0 / 4;       // row 64 s + lane: + 64 s kb
   const int8_t *cl[MF];
@@ -1989,7 +1996,7 @@ void tgemm_skinny_dx_split(XArgs a, int32_t *part, int32_t S) {
   const int r = lane & 15, g = lane >> 4;
   // the S splits of a column block are neighbours in the XCD-contiguous
   // order, so they run on one XCD and share its L2 for dC
-  const int32_t b = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x);
+  const int32_t b = xcd_tile((int32_t)blockIdx.x, (int32_t)gridDim.x, a.xcds);
   const int32_t blk = b / S, sp = b % S;
   const int32_t k0 = blk * sxs::kBK;
   const int64_t kb = a.K / 4;
@@ -2086,6 +2093,401 @@ __global__ __launch_bounds__(256) void skinny_dx_sum(const v4i *__restrict__ par
   }
 }
 
+// ---------------------------------------------------------------------------
+// Double-buffered forward kernel (tgemm_dbuf): C[M][N] = A x W for outputs
+// with enough 256 x 96 tiles for a persistent grid, K % 256 == 0 and
+// K >= 1024.
+//
+// At the "500m" shapes [P10425 "Throughput"] the int32 output is nine tenths
+// of the bytes the product moves, so the kernel keeps HBM writing while it
+// computes: each wave holds two accumulator sets, and while it accumulates
+// tile t in one it stores tile t - 1 from the other, three registers per
+// step over the first sixteen steps of tile t.
+//
+// A workgroup of 8 waves (two per SIMD) owns a 256 x 96 tile; wave w
+// computes rows 32 w .. 32 w + 31 and all 96 columns, as 1 x 3 fragments of
+// 32 x 32 (v_mfma_i32_32x32x32_i8).
+//   A: straight into registers, three steps ahead, by buffer loads of 16
+//      rows x 64 bytes (lane l: row l % 16, 16-byte chunk l / 16).  One
+//      v_permlane16_swap per dword pair of the fragment's two 16-row halves
+//      gives lane l row l % 32 with chunk u + 2 (l / 32), for sub-step u
+//      (the two 32-deep MFMAs of a 64-step).
+//   W: the packed codes of a stage (four steps, 1536 dwords: three per lane)
+//      are loaded three stages ahead and decoded once per tile load
+//      [P10425 "What this adds"], two stages ahead, one dword per lane in
+//      each of the stage's first three steps, into one of three LDS buffers
+//      shared by the eight waves: per step, column n holds 64 bytes with
+//      chunk c at slot c ^ ((n >> 2) & 3), so that the fragment reads (16
+//      columns per 16 lanes, one chunk) and the decode writes (4 columns x 4
+//      chunks per 16 lanes) touch all 64 banks once.  Fragments take the
+//      same chunk per lane as A's.  With three buffers a wave reads the next
+//      stage's fragments before the barrier that ends the current stage.
+//      Nothing in a step depends on the wave's index, so each step is one
+//      basic block and its MFMAs interleave with the rest.
+//   MFMA: A as the instruction's first operand (rows of C), W as its second
+//      (columns): register r of lane l holds C[8 (r / 4) + 4 (l / 32) + r %
+//      4][l % 32] of a fragment, so one dword store writes two 128-byte row
+//      segments.
+//   Edges: each tile reads A and W through buffer resources based at its
+//      first row / column and ending at the operand's end, so rows and
+//      columns past the output read zeros (code 0 is weight 0).  A store
+//      carries its whole offset in the range-checked voffset: rows past the
+//      output fall past the C resource's end, and lanes of columns past it
+//      add their offset to 2^31; nothing outside C is written.
+// The contraction is reduced serially in registers, in int32, exactly.
+// ---------------------------------------------------------------------------
+namespace db {
+constexpr int kWaves = 8, kNT = 64 * kWaves;
+constexpr int BM = 256, BN = 96, TM = 32;
+constexpr int JG = BN / 32;                           // 32-column fragments of a wave
+constexpr int SS = 4;                                 // steps (of 64) per stage
+constexpr int kStepB = BN * BK;                       // decoded bytes of one step
+constexpr int kStageB = SS * kStepB;
+constexpr int kBufs = 3;
+constexpr int kLds = kBufs * kStageB;
+constexpr int kDwStep = BN * (BK / 16);               // packed dwords of one step
+constexpr int kPw = SS * BN * (BK / 16) / kNT;       // packed dwords per thread per stage
+constexpr int D = 3;                                  // A prefetch distance (steps)
+constexpr int kRing = D + 1;
+constexpr int kItSteps = SS;                          // steps per loop iteration (one stage)
+constexpr int kSpreadIt = 4;                          // iterations carrying the previous tile's stores
+constexpr int kAcc = JG * 16;                         // accumulator registers of one set
+constexpr int kStSteps = kSpreadIt * kItSteps;        // steps that carry stores
+constexpr int kStPerStep = kAcc / kStSteps;
+constexpr int kMinStages = kSpreadIt;                 // stages per tile, at least
+constexpr int kRsrcFlags = 0x00020000;                // raw buffer resource, 32-bit data format
+static_assert(kRing == kItSteps, "A ring period = loop iteration");
+static_assert(kStPerStep * kStSteps == kAcc, "stores spread evenly");
+static_assert(kPw * kNT == SS * kDwStep && kPw == SS - 1, "packed dwords: one per lane in each of a stage's first steps");
+}  // namespace db
+
+typedef int32_t v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+struct DbArgs {
+  const int8_t *A;
+  const uint8_t *Wp;
+  int32_t *C;
+  int32_t M, N, K, kb;           // kb = K / 4, the packed row stride
+  int32_t tiles_c, tiles;
+  int32_t nsteps, nst;           // K / 64, K / 256
+  int32_t xcds;                  // workgroup b runs on XCD b % xcds
+};
+
+__device__ __forceinline__ Rsrc db_rsrc(const void *base, int64_t off, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base)) + off, 0,
+                                           (int32_t)(bytes > 0 ? bytes : 0), db::kRsrcFlags);
+}
+
+// the buffer resources of a tile's A rows and W columns (a tile that does
+// not exist gets empty resources: its loads read zeros from nowhere), and of
+// its C block
+__device__ __forceinline__ Rsrc db_rsrc_a(const DbArgs &a, int32_t pos, bool valid) {
+  const int32_t m0 = pos / a.tiles_c * db::BM;
+  return db_rsrc(a.A, (int64_t)m0 * a.K, valid ? (int64_t)(a.M - m0) * a.K : 0);
+}
+__device__ __forceinline__ Rsrc db_rsrc_w(const DbArgs &a, int32_t pos, bool valid) {
+  const int32_t n0 = pos % a.tiles_c * db::BN;
+  return db_rsrc(a.Wp, (int64_t)n0 * a.kb, valid ? (int64_t)(a.N - n0) * a.kb : 0);
+}
+__device__ __forceinline__ Rsrc db_rsrc_c(const DbArgs &a, int32_t pos) {
+  const int32_t m0 = pos / a.tiles_c * db::BM, n0 = pos % a.tiles_c * db::BN;
+  return db_rsrc(a.C, ((int64_t)m0 * a.N + n0) * 4, ((int64_t)(a.M - m0) * a.N - n0) * 4);
+}
+
+// Loads run ahead of the computation through two cursors: A's (a step: its
+// resource and byte offset) and W's (a stage).  Each moves on to the next
+// tile's resource at the end of the current tile's contraction.
+struct DbCursor {
+  Rsrc r;
+  int32_t off;
+};
+
+struct DbState {
+  // per lane
+  uint32_t voffA[2];             // A load h: row 32 w + 16 h + l % 16, chunk l / 16
+  uint32_t voffW[db::kPw];       // packed dword of a stage
+  uint32_t ldsWr[db::kPw];       // its decoded chunk in a stage buffer
+  uint32_t ldsRd[2];             // fragment read of sub-step u in a stage buffer
+  uint32_t sbase[db::JG];        // store offsets of the tile being stored (past 2^31: column past N)
+  // uniform
+  DbCursor ca, cw;               // next A step / W stage to load
+  Rsrc na, nw;                   // the next tile's A and W resources
+  Rsrc pc;                       // C resource of the tile being stored
+  int32_t G;                     // global stage counter of the current stage
+  int32_t wave;
+};
+
+struct DbRing {   // A loads in flight: [slot][half]
+  v4u x[db::kRing][2];
+};
+
+// issue the A loads of the cursor's step into ring slot SLOT, then advance
+template <int SLOT>
+__device__ __forceinline__ void db_load_a(DbRing &ring, DbState &st, const DbArgs &a) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    ring.x[SLOT][h] = __builtin_amdgcn_raw_buffer_load_b128(st.ca.r, st.voffA[h], st.ca.off, 0);
+  st.ca.off += BK;
+  if (st.ca.off == a.K) {
+    st.ca.off = 0;
+    st.ca.r = st.na;
+  }
+}
+
+// issue the packed W loads of the cursor's stage, then advance
+__device__ __forceinline__ void db_load_w(uint32_t (&pw)[db::kPw], DbState &st, const DbArgs &a) {
+#pragma unroll
+  for (int i = 0; i < db::kPw; ++i) pw[i] = __builtin_amdgcn_raw_buffer_load_b32(st.cw.r, st.voffW[i], st.cw.off, 0);
+  st.cw.off += db::SS * (BK / 4);
+  if (st.cw.off == a.kb) {
+    st.cw.off = 0;
+    st.cw.r = st.nw;
+  }
+}
+
+// register q of an accumulator set: fragment jg, register r, and the
+// fragment-local row of lanes 0..31 (lanes 32..63 hold row + 4)
+template <int Q>
+struct DbIdx {
+  static constexpr int jg = Q / 16, r = Q % 16;
+  static constexpr int row = 8 * (r / 4) + r % 4;
+};
+
+template <int Q>
+__device__ __forceinline__ void db_store1(const v16i (&accp)[db::JG], const DbState &st, int32_t N4) {
+  typedef DbIdx<Q> I;
+  const uint32_t voff = st.sbase[I::jg] + (uint32_t)(I::row * N4);
+  __builtin_amdgcn_raw_buffer_store_b32(accp[I::jg][I::r], st.pc, voff, 0, 0);
+}
+
+template <int Q, int E>
+__device__ __forceinline__ void db_stores(const v16i (&accp)[db::JG], const DbState &st, int32_t N4) {
+  if constexpr (E > 0) {
+    db_store1<Q>(accp, st, N4);
+    db_stores<Q + 1, E - 1>(accp, st, N4);
+  }
+}
+
+__device__ __forceinline__ void db_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// the packed dword i of this lane, decoded into stage buffer dst
+template <int I>
+__device__ __forceinline__ void db_decode(const uint32_t (&pw)[db::kPw], const DbState &st, int8_t *dst) {
+  *reinterpret_cast<v4i *>(dst + st.ldsWr[I]) = decode16(pw[I]);
+}
+
+// One step S of the tile (ring slot and step of the stage SLOT, fragments
+// wf[SLOT % 2]; S < 0: a step past the ones that carry stores): issues the
+// A loads D steps ahead, forms the step's A fragments, reads the W fragments
+// of the next step, runs the 6 MFMAs, decodes this lane's dword SLOT of the
+// packed codes of stage G + 2 and, with STORE, registers 3 S .. 3 S + 2 of
+// the previous tile.  FIRST: the tile's first step (accumulators start at
+// 0).  The instruction order inside a step is fixed by scheduling groups, so
+// that the MFMAs issue back to back with the other work in between.
+template <int SLOT, int S, bool FIRST, bool STORE>
+__device__ __forceinline__ void db_step(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
+                                        v4i (&wf)[2][db::JG][2], const uint32_t (&pw)[db::kPw], DbState &st,
+                                        const DbArgs &a, int8_t *smem) {
+  using namespace db;
+  constexpr int P = SLOT % 2;            // fragment set of this step
+  __builtin_amdgcn_sched_barrier(0);
+  db_load_a<(SLOT + D) % kRing>(ring, st, a);
+  v4i af[2];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const v2u p = __builtin_amdgcn_permlane16_swap(ring.x[SLOT][0][d], ring.x[SLOT][1][d], false, false);
+    af[0][d] = (int32_t)p[0];
+    af[1][d] = (int32_t)p[1];
+  }
+  {
+    // fragments of the next step: this stage's next step, or the next
+    // stage's first (decoded during the previous stage, published by its
+    // barrier)
+    constexpr bool last = SLOT == SS - 1;
+    const int32_t buf = (last ? st.G + 1 : st.G) % kBufs;
+    const int8_t *base = smem + buf * kStageB + (last ? 0 : (SLOT + 1) * kStepB);
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        wf[1 - P][jg][u] = *reinterpret_cast<const v4i *>(base + st.ldsRd[u] + jg * 32 * BK);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg)
+      acc[jg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[u], wf[P][jg][u], (FIRST && u == 0) ? v16i{} : acc[jg],
+                                                      0, 0, 0);
+  if constexpr (SLOT < kPw) db_decode<SLOT>(pw, st, smem + ((st.G + 2) % kBufs) * kStageB);
+  if constexpr (STORE && S >= 0 && S < kStSteps) db_stores<S * kStPerStep, kStPerStep>(accp, st, 4 * a.N);
+  // order: the A loads, the swaps, then each MFMA followed by a share of the
+  // VALU work, an LDS access and a memory access
+  __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // A loads
+  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // swaps
+#pragma unroll
+  for (int k = 0; k < 2 * JG; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // VALU
+    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0); // LDS
+    __builtin_amdgcn_sched_group_barrier(0x040, 1, 0); // store
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage (four steps), global stage st.G: pw[0] holds the packed codes
+// of stage G + 2 (decoded during this stage), pw[1] those of G + 3 (in
+// flight); at the end pw[1] moves to pw[0] and the stage after goes out.
+// IT < 0: an iteration past the ones that carry stores.
+template <bool FIRST, bool STORE, int IT>
+__device__ __forceinline__ void db_iter(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
+                                        v4i (&wf)[2][db::JG][2], uint32_t (&pw)[2][db::kPw], DbState &st,
+                                        const DbArgs &a, int8_t *smem) {
+  using namespace db;
+  constexpr int s0 = IT < 0 ? -100 : IT * kItSteps;
+  db_step<0, s0, FIRST, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
+  db_step<1, s0 + 1, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
+  db_step<2, s0 + 2, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
+  db_step<3, s0 + 3, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
+#pragma unroll
+  for (int i = 0; i < kPw; ++i) pw[0][i] = pw[1][i];
+  db_load_w(pw[1], st, a);
+  db_barrier();
+  st.G += 1;
+}
+
+// a whole tile: the first four iterations carry the previous tile's stores
+template <bool STORE>
+__device__ __forceinline__ void db_run_tile(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
+                                            v4i (&wf)[2][db::JG][2], uint32_t (&pw)[2][db::kPw], DbState &st,
+                                            const DbArgs &a, int8_t *smem) {
+  using namespace db;
+  static_assert(kSpreadIt == 4, "unrolled spread");
+  db_iter<true, STORE, 0>(acc, accp, ring, wf, pw, st, a, smem);
+  db_iter<false, STORE, 1>(acc, accp, ring, wf, pw, st, a, smem);
+  db_iter<false, STORE, 2>(acc, accp, ring, wf, pw, st, a, smem);
+  db_iter<false, STORE, 3>(acc, accp, ring, wf, pw, st, a, smem);
+  for (int32_t s0 = kSpreadIt * kItSteps; s0 < a.nsteps; s0 += kItSteps)
+    db_iter<false, false, -1>(acc, accp, ring, wf, pw, st, a, smem);
+}
+
+// the tile at position pos, just computed, becomes the one being stored;
+// the loads run on into the tile at pos_after (if there is one: has_after)
+__device__ __forceinline__ void db_advance(DbState &st, const DbArgs &a, int32_t lane, int32_t pos,
+                                           int32_t pos_after, bool has_after) {
+  using namespace db;
+  st.pc = db_rsrc_c(a, pos);
+  const int32_t n0 = pos % a.tiles_c * BN, h = lane >> 5, c = lane & 31;
+#pragma unroll
+  for (int jg = 0; jg < JG; ++jg) {
+    const int32_t col = 32 * jg + c;
+    st.sbase[jg] = n0 + col < a.N ? (uint32_t)(((TM * st.wave + 4 * h) * a.N + col) * 4)
+                                  : 0x80000000u + (uint32_t)(col * 4);
+  }
+  st.na = db_rsrc_a(a, pos_after, has_after);
+  st.nw = db_rsrc_w(a, pos_after, has_after);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(db::kNT, db::kNT), amdgpu_waves_per_eu(2, 2)))
+void tgemm_dbuf(DbArgs a) {
+  using namespace db;
+  __builtin_assume(a.nst >= kMinStages && a.nsteps == SS * a.nst && a.K == BK * a.nsteps && a.kb * 4 == a.K);
+  __shared__ __attribute__((aligned(1024))) int8_t smem[kLds];
+  const int32_t tid = threadIdx.x, lane = tid & 63;
+
+  // tiles of this workgroup: the row-major tile positions are split into one
+  // contiguous run per XCD; the nx workgroups of an XCD take every nx-th
+  // position of its run, so the tiles an XCD works on at one time share A
+  // rows (and all of W) in its L2
+  const int32_t xcds = a.xcds, nx = (int32_t)gridDim.x / xcds;
+  const int32_t xcd = (int32_t)blockIdx.x % xcds, j0 = (int32_t)blockIdx.x / xcds;
+  const int32_t qx = a.tiles / xcds, rx = a.tiles % xcds;
+  const int32_t start = xcd * qx + (xcd < rx ? xcd : rx) + j0;
+  const int32_t cnt = qx + (xcd < rx ? 1 : 0);
+  const int32_t ntile = cnt > j0 ? (cnt - j0 + nx - 1) / nx : 0;
+  if (ntile == 0) return;
+
+  DbState st;
+  st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    st.voffA[h] = (uint32_t)((TM * st.wave + 16 * h + (lane & 15)) * a.K + 16 * (lane >> 4));
+#pragma unroll
+  for (int i = 0; i < kPw; ++i) {
+    const int32_t p = tid + kNT * i, sx = p / kDwStep, rem = p % kDwStep, n = rem >> 2, c = rem & 3;
+    st.voffW[i] = (uint32_t)(n * a.kb + 16 * sx + 4 * c);
+    st.ldsWr[i] = (uint32_t)(sx * kStepB + n * BK + 16 * (c ^ ((n >> 2) & 3)));
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int32_t n = lane & 31, c = u + 2 * (lane >> 5);
+    st.ldsRd[u] = (uint32_t)(n * BK + 16 * (c ^ ((n >> 2) & 3)));
+  }
+#pragma unroll
+  for (int jg = 0; jg < JG; ++jg) st.sbase[jg] = 0x80000000u;
+  st.ca.r = db_rsrc_a(a, start, true);
+  st.cw.r = db_rsrc_w(a, start, true);
+  st.ca.off = 0;
+  st.cw.off = 0;
+  st.na = db_rsrc_a(a, start + nx, ntile > 1);
+  st.nw = db_rsrc_w(a, start + nx, ntile > 1);
+  st.pc = db_rsrc_c(a, start);
+  st.G = 0;
+
+  // prologue: A steps 0 .. D - 1 in flight; stages 0 and 1 decoded into
+  // buffers 0 and 1; packed stages 2 and 3 in flight; fragments of step 0
+  DbRing ring;
+  v4i wf[2][JG][2];
+  uint32_t pw[2][kPw];
+  db_load_w(pw[0], st, a);
+  db_load_w(pw[1], st, a);
+  db_load_a<0>(ring, st, a);
+  db_load_a<1>(ring, st, a);
+  db_load_a<2>(ring, st, a);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    db_decode<0>(pw[b], st, smem + b * kStageB);
+    db_decode<1>(pw[b], st, smem + b * kStageB);
+    db_decode<2>(pw[b], st, smem + b * kStageB);
+  }
+  db_load_w(pw[0], st, a);
+  db_load_w(pw[1], st, a);
+  db_barrier();
+#pragma unroll
+  for (int jg = 0; jg < JG; ++jg)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) wf[0][jg][u] = *reinterpret_cast<const v4i *>(smem + st.ldsRd[u] + jg * 32 * BK);
+
+  v16i acc0[JG], acc1[JG];
+  db_run_tile<false>(acc0, acc1, ring, wf, pw, st, a, smem);
+  int32_t pos = start;
+  for (int32_t it = 1;; it += 2) {
+    if (it >= ntile) {
+      db_advance(st, a, lane, pos, pos, false);
+      db_stores<0, kAcc>(acc0, st, 4 * a.N);
+      break;
+    }
+    db_advance(st, a, lane, pos, pos + 2 * nx, it + 1 < ntile);
+    pos += nx;
+    db_run_tile<true>(acc1, acc0, ring, wf, pw, st, a, smem);
+    if (it + 1 >= ntile) {
+      db_advance(st, a, lane, pos, pos, false);
+      db_stores<0, kAcc>(acc1, st, 4 * a.N);
+      break;
+    }
+    db_advance(st, a, lane, pos, pos + 2 * nx, it + 2 < ntile);
+    pos += nx;
+    db_run_tile<true>(acc0, acc1, ring, wf, pw, st, a, smem);
+  }
+  // loads past the last tile (of empty resources) and the stores complete
+  // before the wave ends
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -2107,20 +2509,53 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 // (A variant that loads the int8 operand of the forward and dX straight into
 // MFMA registers, without LDS, measured no faster in the three-product step
 // on MI355X and was left out.)
-enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3, KSKINNY = 4 };
+enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3, KSKINNY = 4, KDBUF = 5 };
+
+// The machine the plans are made for: compute units (one persistent
+// workgroup each) and XCDs (workgroup b runs on XCD b % xcds, each XCD with
+// its own L2).  The calls query the current device once and keep the answer;
+// the host-only plan query takes MI355X's values unless given others.
+struct Machine {
+  int32_t cus, xcds;
+};
+constexpr Machine kMI355X = {256, 8};
+
+bool machine_ok(const Machine &mc) { return mc.cus >= 1 && mc.xcds >= 1 && mc.cus % mc.xcds == 0; }
+
+int query_machine(Machine *out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TGEMM_ERR_HIP;
+  constexpr int kMaxDev = 64;
+  static std::atomic<uint64_t> cache[kMaxDev];
+  uint64_t v = dev < kMaxDev ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return TGEMM_ERR_HIP;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 ||
+        cus % xcds != 0)
+      xcds = 1;
+    v = ((uint64_t)(uint32_t)cus << 32) | (uint32_t)xcds;
+    if (dev < kMaxDev) cache[dev].store(v, std::memory_order_relaxed);
+  }
+  out->cus = (int32_t)(v >> 32);
+  out->xcds = (int32_t)(uint32_t)v;
+  return TGEMM_OK;
+}
+
 
 // The streaming kernels (forward, dX): apply when the contraction is a whole
 // number of steps, the operands are aligned for their 16- and 4-byte loads
 // (dX: packed columns in whole dwords, K % 16 == 0), their 32-bit offsets
 // cannot overflow, and the output has enough tiles for a full persistent grid.
-constexpr int kStreamCUs = 256;  // MI355X compute units: one workgroup each
 
 struct StreamPlan {
   bool ok;
   int32_t bn, tiles_r, tiles_c, tiles, grid, lds;
 };
 
-StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
+                       const Machine &mc) {
   StreamPlan sp{};
   if (op == DW || qalign % 16 != 0 || walign % 4 != 0) return sp;
   const Shape s = shape_of(op, M, N, K);
@@ -2129,12 +2564,12 @@ StreamPlan stream_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
   sp.bn = op == FWD ? fs::Geo<FWD>::BN : fs::Geo<DX>::BN;
   sp.lds = op == FWD ? fs::Geo<FWD>::kLds : fs::Geo<DX>::kLds;
   const int64_t tr = ceil_div(s.R, fs::BM), tc = ceil_div(s.Cc, sp.bn);
-  if (tr * tc < kStreamCUs) return sp;
+  if (tr * tc < mc.cus || !machine_ok(mc)) return sp;
   sp.ok = true;
   sp.tiles_r = (int32_t)tr;
   sp.tiles_c = (int32_t)tc;
   sp.tiles = (int32_t)(tr * tc);
-  sp.grid = kStreamCUs;
+  sp.grid = mc.cus;
   return sp;
 }
 
@@ -2149,12 +2584,14 @@ struct SkinnyPlan {
   int32_t mf, nb, grid, lds;
 };
 
-SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
+                       const Machine &mc) {
   SkinnyPlan kp{};
   if (op != FWD || M > 32 || K % 64 != 0 || qalign % 16 != 0 || walign % 16 != 0) return kp;
   if (N > INT32_MAX - 64 || K > INT32_MAX) return kp;
   kp.mf = M > 16 ? 2 : 1;
-  kp.nb = N >= 128 * 64 ? 4 : N >= 128 * 32 ? 2 : 1;
+  const int64_t half = mc.cus / 2 > 0 ? mc.cus / 2 : 1;   // workgroups wanted, at least
+  kp.nb = N >= half * 64 ? 4 : N >= half * 32 ? 2 : 1;
   kp.al = M > 8;
   kp.grid = (int32_t)ceil_div(N, 16 * kp.nb);
   const int32_t red = sk::kWaves * 16 * kp.mf * (4 * kp.nb + 1) * 16;
@@ -2167,12 +2604,13 @@ SkinnyPlan skinny_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign
 // The skinny dX: at most 32 rows, N % 64 == 0 (whole contraction steps),
 // K % 16 == 0, 16-byte aligned dC, and Wpacked aligned for the per-row
 // loads.  Column blocks of 64 (K % 64 == 0 and 128 or more of them) or 16.
-SkinnyPlan skinny_dx_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+SkinnyPlan skinny_dx_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
+                          const Machine &mc) {
   SkinnyPlan kp{};
   if (op != DX || M > 32 || N % 64 != 0 || K % 16 != 0 || qalign % 16 != 0) return kp;
   if (N > INT32_MAX || K > INT32_MAX - 64) return kp;
   kp.mf = M > 16 ? 2 : 1;
-  kp.nb = (K % 64 == 0 && K / 64 >= 128) ? 4 : 1;
+  kp.nb = (K % 64 == 0 && K / 64 >= mc.cus / 2) ? 4 : 1;
   if (walign % (4 * kp.nb) != 0) return kp;
   kp.al = false;
   kp.grid = (int32_t)(K / (16 * kp.nb));
@@ -2193,13 +2631,14 @@ struct SplitDxPlan {
   int32_t mf, blocks, S, grid;
   int64_t bytes;      // workspace: S partial sums of M x K int32
 };
-SplitDxPlan skinny_dx_split_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign) {
+SplitDxPlan skinny_dx_split_plan(int op, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
+                                 const Machine &mc) {
   SplitDxPlan xp{};
   if (op != DX || M > 32 || N % 64 != 0 || K % sxs::kBK != 0 || qalign % 16 != 0 || walign % 16 != 0)
     return xp;
   if (N > INT32_MAX || K > INT32_MAX - 64) return xp;
   const int64_t blocks = K / sxs::kBK, nsteps = N / 64;
-  const int64_t S = (256 + blocks - 1) / blocks;
+  const int64_t S = (mc.cus + blocks - 1) / blocks;
   if (S < 2 || nsteps < sk::kWaves * S) return xp;
   xp.mf = M > 16 ? 2 : 1;
   xp.blocks = (int32_t)blocks;
@@ -2221,12 +2660,40 @@ void launch_skinny(const KArgs &ka, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_skinny<MF, NB, AL>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
 }
 
+// The double-buffered forward (tgemm_dbuf): int32 output, K % 256 == 0 and
+// K >= 1024 (whole four-step stages, at least the four stages that carry
+// the previous tile's stores), 16-byte aligned A, 4-byte aligned Wpacked and
+// C, 32-bit buffer offsets (C with its rows rounded up to whole tiles), and
+// at least four 256 x 96 tiles per CU, so that most of the stores overlap a
+// later tile's computation.
+struct DbPlan {
+  bool ok;
+  int32_t tiles_c, tiles, grid, xcds;
+};
+
+DbPlan dbuf_plan(int op, int kind, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
+                 uintptr_t oalign, const Machine &mc) {
+  DbPlan d{};
+  if (op != FWD || kind != OUT_I32 || !machine_ok(mc)) return d;
+  if (K % (db::SS * BK) != 0 || K / (db::SS * BK) < db::kMinStages) return d;
+  if (qalign % 16 != 0 || walign % 4 != 0 || oalign % 4 != 0) return d;
+  const int64_t tr = ceil_div(M, db::BM), tc = ceil_div(N, db::BN);
+  if (M > INT32_MAX / K || N > INT32_MAX / (K / 4) || tr * db::BM > INT32_MAX / (4 * N)) return d;
+  if (tr * tc < 4 * (int64_t)mc.cus || tr * tc > INT32_MAX) return d;
+  d.ok = true;
+  d.tiles_c = (int32_t)tc;
+  d.tiles = (int32_t)(tr * tc);
+  d.grid = mc.cus;
+  d.xcds = mc.xcds;
+  return d;
+}
+
 // the contraction split between two halves of a workgroup: dW on the
 // 128 x 144 tile, and dX on that tile when its tiles do not fill the CUs;
 // at least 8 steps
-int pick_kernel(int op, int tile, int64_t L, int64_t tiles) {
+int pick_kernel(int op, int tile, int64_t L, int64_t tiles, const Machine &mc) {
   if (op == DW && tile == TW && L >= 8 * BK) return KSPLIT;
-  if (op == DX && tile == TW && L >= 8 * BK && tiles <= 256) return KSPLIT;
+  if (op == DX && tile == TW && L >= 8 * BK && tiles <= mc.cus) return KSPLIT;
   return KTILED;
 }
 
@@ -2289,6 +2756,8 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
       (overlaps(ws, ws_bytes, q, qbytes) || overlaps(ws, ws_bytes, p, pbytes) ||
        overlaps(ws, ws_bytes, out, obytes) || (kind != OUT_I32 && overlaps(ws, ws_bytes, rs, s.R * 4))))
     return TGEMM_ERR_ALIAS;
+  Machine mc;
+  if (query_machine(&mc) != TGEMM_OK) return TGEMM_ERR_HIP;
   Out o;
   o.ptr = out;
   o.rs = rs;
@@ -2298,7 +2767,7 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   o.vec = (s.Cc % 4 == 0 && aligned(out, 4 * esz)) ? 1 : 0;
   o.vec8 = (kind == OUT_BF16 && s.Cc % 8 == 0 && aligned(out, 16)) ? 1 : 0;
 
-  const int tile = pick_tile(s);
+  const int tile = pick_tile(s, mc.cus);
   const TileInfo &ti = kTileInfo[tile];
   Args a;
   a.q = q;
@@ -2311,13 +2780,35 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   a.ldp = op == DW ? N : K / 4;
   a.tiles_c = (int32_t)ceil_div(s.Cc, ti.bn);
   a.tiles = (int32_t)(ceil_div(s.R, ti.bm) * a.tiles_c);
-  a.band_cols = pick_band_cols(op, M, N, K, a.tiles_c);
+  a.band_cols = pick_band_cols(op, M, N, K, a.tiles_c, mc.xcds);
+  a.xcds = mc.xcds;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
   {
-    const SkinnyPlan kp = skinny_plan(op, M, N, K, align_of(q), align_of(p));
+    const DbPlan d = dbuf_plan(op, kind, M, N, K, align_of(q), align_of(p), align_of(out), mc);
+    if (d.ok) {
+      DbArgs da;
+      da.A = q;
+      da.Wp = static_cast<const uint8_t *>(p);
+      da.C = static_cast<int32_t *>(out);
+      da.M = (int32_t)M;
+      da.N = (int32_t)N;
+      da.K = (int32_t)K;
+      da.kb = (int32_t)(K / 4);
+      da.tiles_c = d.tiles_c;
+      da.tiles = d.tiles;
+      da.nsteps = (int32_t)(K / BK);
+      da.nst = (int32_t)(K / (db::SS * BK));
+      da.xcds = d.xcds;
+      hipLaunchKernelGGL(tgemm_dbuf, dim3(d.grid), dim3(db::kNT), 0, stream, da);
+      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+    }
+  }
+  {
+    const SkinnyPlan kp = skinny_plan(op, M, N, K, align_of(q), align_of(p), mc);
     if (kp.ok) {
       KArgs ka;
+      ka.xcds = mc.xcds;
       ka.A = q;
       ka.Wp = static_cast<const uint8_t *>(p);
       ka.o = o;
@@ -2344,9 +2835,10 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
   {
-    const SplitDxPlan xp = skinny_dx_split_plan(op, M, N, K, align_of(q), align_of(p));
+    const SplitDxPlan xp = skinny_dx_split_plan(op, M, N, K, align_of(q), align_of(p), mc);
     if (xp.ok && ws && ws_bytes >= xp.bytes && aligned(ws, 16)) {
       XArgs xa;
+      xa.xcds = mc.xcds;
       xa.dC = q;
       xa.Wp = static_cast<const uint8_t *>(p);
       xa.o = o;
@@ -2367,9 +2859,10 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
   {
-    const SkinnyPlan kp = skinny_dx_plan(op, M, N, K, align_of(q), align_of(p));
+    const SkinnyPlan kp = skinny_dx_plan(op, M, N, K, align_of(q), align_of(p), mc);
     if (kp.ok) {
       XArgs xa;
+      xa.xcds = mc.xcds;
       xa.dC = q;
       xa.Wp = static_cast<const uint8_t *>(p);
       xa.o = o;
@@ -2385,9 +2878,10 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
   {
-    const StreamPlan sp = stream_plan(op, M, N, K, align_of(q), align_of(p));
+    const StreamPlan sp = stream_plan(op, M, N, K, align_of(q), align_of(p), mc);
     if (sp.ok) {
       SArgs sa;
+      sa.xcds = mc.xcds;
       sa.Q = q;
       sa.Wp = static_cast<const uint8_t *>(p);
       sa.o = o;
@@ -2407,7 +2901,7 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
     }
   }
 
-  const int kernel = pick_kernel(op, tile, s.L, a.tiles);
+  const int kernel = pick_kernel(op, tile, s.L, a.tiles, mc);
   hipError_t e;
   if (op == FWD)
     e = launch_op<FWD>(a, kernel, tile, fast, stream);
@@ -2461,7 +2955,10 @@ int ternary_gemm_dx_workspace(int64_t M, int64_t N, int64_t K, int64_t align, in
   const int st = check_dims(DX, M, N, K);
   if (st != TGEMM_OK) return st;
   const uintptr_t al = align > 0 ? (uintptr_t)align : 1;
-  const SplitDxPlan xp = skinny_dx_split_plan(DX, M, N, K, al, al);
+  // the machine the calls will run on: the current device, else MI355X
+  Machine mc = kMI355X;
+  if (query_machine(&mc) != TGEMM_OK) mc = kMI355X;
+  const SplitDxPlan xp = skinny_dx_split_plan(DX, M, N, K, al, al, mc);
   *bytes = xp.ok ? xp.bytes : 0;
   return TGEMM_OK;
 }
@@ -2505,8 +3002,21 @@ const char *ternary_gemm_status_str(int status) {
   }
 }
 
-int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tgemm_plan *plan) {
+int ternary_gemm_machine(int32_t *cus, int32_t *xcds) {
+  if (!cus || !xcds) return TGEMM_ERR_NULL;
+  Machine mc;
+  const int st = query_machine(&mc);
+  if (st != TGEMM_OK) return st;
+  *cus = mc.cus;
+  *xcds = mc.xcds;
+  return TGEMM_OK;
+}
+
+int ternary_gemm_plan_on(int op, int64_t M, int64_t N, int64_t K, int64_t align, int32_t cus, int32_t xcds,
+                         tgemm_plan *plan) {
   if (!plan) return TGEMM_ERR_NULL;
+  const Machine mc = {cus, xcds};
+  if (!machine_ok(mc)) return TGEMM_ERR_DIM;
   const int st = check_dims(op, M, N, K);
   if (st != TGEMM_OK) return st;
   const Shape s = shape_of(op, M, N, K);
@@ -2516,9 +3026,25 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
   plan->out_cols = s.Cc;
   plan->contraction = s.L;
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
+  plan->xcds = mc.xcds;
   {
-    SkinnyPlan kp = skinny_plan(op, M, N, K, al, al);
-    if (!kp.ok) kp = skinny_dx_plan(op, M, N, K, al, al);
+    const DbPlan d = dbuf_plan(op, OUT_I32, M, N, K, al, al, al, mc);
+    if (d.ok) {
+      plan->tile_rows = db::BM;
+      plan->tile_cols = db::BN;
+      plan->tiles = d.tiles;
+      plan->workgroups = d.grid;
+      plan->tiles_per_workgroup = ceil_div(ceil_div(d.tiles, mc.xcds), d.grid / mc.xcds);
+      plan->band_cols = d.tiles_c;
+      plan->kernel = KDBUF;
+      plan->threads_per_workgroup = db::kNT;
+      plan->lds_bytes = db::kLds;
+      return TGEMM_OK;
+    }
+  }
+  {
+    SkinnyPlan kp = skinny_plan(op, M, N, K, al, al, mc);
+    if (!kp.ok) kp = skinny_dx_plan(op, M, N, K, al, al, mc);
     if (kp.ok) {
       plan->tile_rows = 16 * kp.mf;
       plan->tile_cols = 16 * kp.nb;
@@ -2533,13 +3059,13 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
     }
   }
   {
-    const StreamPlan sp = stream_plan(op, M, N, K, al, al);
+    const StreamPlan sp = stream_plan(op, M, N, K, al, al, mc);
     if (sp.ok) {
       plan->tile_rows = fs::BM;
       plan->tile_cols = sp.bn;
       plan->tiles = sp.tiles;
       plan->workgroups = sp.grid;
-      plan->tiles_per_workgroup = ceil_div(ceil_div(sp.tiles, 8), sp.grid / 8);
+      plan->tiles_per_workgroup = ceil_div(ceil_div(sp.tiles, mc.xcds), sp.grid / mc.xcds);
       plan->band_cols = sp.tiles_c;
       plan->kernel = KSTREAM;
       plan->threads_per_workgroup = fs::kNT;
@@ -2547,18 +3073,22 @@ int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tg
       return TGEMM_OK;
     }
   }
-  const int tile = pick_tile(s);
+  const int tile = pick_tile(s, mc.cus);
   const TileInfo &ti = kTileInfo[tile];
   plan->tile_rows = ti.bm;
   plan->tile_cols = ti.bn;
   plan->tiles = ceil_div(s.R, ti.bm) * ceil_div(s.Cc, ti.bn);
   plan->workgroups = plan->tiles;
   plan->tiles_per_workgroup = 1;
-  plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn));
-  plan->kernel = pick_kernel(op, tile, s.L, plan->tiles);
+  plan->band_cols = pick_band_cols(op, M, N, K, (int32_t)ceil_div(s.Cc, ti.bn), mc.xcds);
+  plan->kernel = pick_kernel(op, tile, s.L, plan->tiles, mc);
   plan->threads_per_workgroup = plan->kernel == KSPLIT ? 2 * kThreads : kThreads;
   plan->lds_bytes = kernel_lds(op, plan->kernel, tile);
   return TGEMM_OK;
+}
+
+int ternary_gemm_plan(int op, int64_t M, int64_t N, int64_t K, int64_t align, tgemm_plan *plan) {
+  return ternary_gemm_plan_on(op, M, N, K, align, kMI355X.cus, kMI355X.xcds, plan);
 }
 
 int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iteration, int64_t *row0,
@@ -2566,21 +3096,21 @@ int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iter
   if (!plan || !row0 || !col0) return TGEMM_ERR_NULL;
   if (workgroup < 0 || workgroup >= plan->workgroups || iteration < 0 ||
       iteration >= plan->tiles_per_workgroup || plan->tiles > INT32_MAX || plan->tile_rows < 1 ||
-      plan->tile_cols < 1)
+      plan->tile_cols < 1 || plan->xcds < 1)
     return TGEMM_ERR_DIM;
   const int32_t tiles_c = (int32_t)ceil_div(plan->out_cols, plan->tile_cols);
-  const int32_t tiles = (int32_t)plan->tiles;
+  const int32_t tiles = (int32_t)plan->tiles, xcds = plan->xcds;
   int32_t tr, tc;
-  if (plan->kernel == KSTREAM) {
-    // the kernel's own order: eight contiguous runs of row-major tile
-    // positions, one per XCD; workgroup b (XCD b % 8) takes every nx-th
-    // position of its run, starting at b / 8
-    if (plan->workgroups % 8 != 0) return TGEMM_ERR_DIM;
-    const int32_t nx = (int32_t)plan->workgroups / 8, xcd = (int32_t)(workgroup % 8);
-    const int32_t j = (int32_t)(workgroup / 8);
-    const int32_t q8 = tiles / 8, r8 = tiles % 8;
-    const int32_t start = xcd * q8 + (xcd < r8 ? xcd : r8);
-    const int32_t cnt = q8 + (xcd < r8 ? 1 : 0);
+  if (plan->kernel == KSTREAM || plan->kernel == KDBUF) {
+    // the kernels' own order: one contiguous run of row-major tile positions
+    // per XCD; workgroup b (XCD b % xcds) takes every nx-th position of its
+    // run, starting at b / xcds
+    if (plan->workgroups % xcds != 0) return TGEMM_ERR_DIM;
+    const int32_t nx = (int32_t)plan->workgroups / xcds, xcd = (int32_t)(workgroup % xcds);
+    const int32_t j = (int32_t)(workgroup / xcds);
+    const int32_t qx = tiles / xcds, rx = tiles % xcds;
+    const int32_t start = xcd * qx + (xcd < rx ? xcd : rx);
+    const int32_t cnt = qx + (xcd < rx ? 1 : 0);
     const int64_t pos = j + iteration * nx;
     if (pos >= cnt) return TGEMM_ERR_DIM;
     tr = (int32_t)((start + pos) / tiles_c);
@@ -2589,10 +3119,10 @@ int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iter
     // all rows; the column block in the XCD-contiguous order
     if (iteration != 0) return TGEMM_ERR_DIM;
     tr = 0;
-    tc = xcd_tile((int32_t)workgroup, tiles);
+    tc = xcd_tile((int32_t)workgroup, tiles, xcds);
   } else {
     if (iteration != 0) return TGEMM_ERR_DIM;
-    tile_rc(xcd_tile((int32_t)workgroup, tiles), tiles / tiles_c, tiles_c, plan->band_cols, &tr, &tc);
+    tile_rc(xcd_tile((int32_t)workgroup, tiles, xcds), tiles / tiles_c, tiles_c, plan->band_cols, &tr, &tc);
   }
   *row0 = (int64_t)tr * plan->tile_rows;
   *col0 = (int64_t)tc * plan->tile_cols;

@@ -11,7 +11,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
+from shapes import (DBUF_SHAPES, DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
                     SPLIT_DX_SHAPES, STREAM_SHAPES, TILES)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -95,8 +95,8 @@ def test_alias_rejected():
     assert B.call_raw("ternary_gemm_s8_dw", base, base + 4096, base + 4096, M, N, K) == B.ERR_ALIAS
 
 
-def _coverage(op, M, N, K):
-    pl = B.plan(op, M, N, K)
+def _coverage(op, M, N, K, cus=None, xcds=None):
+    pl = B.plan(op, M, N, K, cus=cus, xcds=xcds)
     seen = []
     for wg in range(pl.workgroups):
         for it in range(pl.tiles_per_workgroup):
@@ -121,12 +121,14 @@ def _coverage(op, M, N, K):
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280), ("dx", 1782, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
     + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES]
+    + [("fwd",) + s for s in DBUF_SHAPES]
     + [("fwd",) + s for s in SKINNY_SHAPES] + [("dx",) + s for s in SKINNY_DX_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.lds_bytes <= 160 * 1024
-    if pl.kernel == B.KERNEL_STREAM:
-        assert pl.threads_per_workgroup == 512 and pl.workgroups == 256
+    if pl.kernel in (B.KERNEL_STREAM, B.KERNEL_DBUF):
+        assert pl.threads_per_workgroup == 512
+        assert pl.workgroups == 256 and pl.xcds == 8
         per_xcd = -(-pl.tiles // 8)
         assert pl.tiles_per_workgroup == -(-per_xcd // 32)
     elif pl.kernel == B.KERNEL_SKINNY:
@@ -141,12 +143,12 @@ def test_parity_shapes_reach_every_tile_and_path():
     # the GPU parity shape lists exercise every tile shape on both load paths,
     # and every kernel on each load path it serves
     kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1),
-                       (B.KERNEL_SKINNY, 1)},
+                       (B.KERNEL_SKINNY, 1), (B.KERNEL_DBUF, 1)},
                "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1), (B.KERNEL_SKINNY, 1),
                       (B.KERNEL_SPLIT, 0), (B.KERNEL_SPLIT, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES),
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES + DBUF_SHAPES),
                        ("dx", DX_SHAPES + DX_STREAM_SHAPES + SKINNY_DX_SHAPES),
                        ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
@@ -161,7 +163,11 @@ def test_parity_shapes_reach_every_tile_and_path():
 
 
 def test_kernel_choice():
-    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
+    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_DBUF
+    assert B.plan("fwd", 16384, 3456, 1408).kernel == B.KERNEL_STREAM   # K % 256 != 0
+    assert B.plan("fwd", 16384, 3456, 768).kernel == B.KERNEL_STREAM    # K < 1024
+    assert B.plan("fwd", 6144, 3456, 1280).kernel == B.KERNEL_STREAM    # 864 tiles of 256 x 96
+    assert B.plan("fwd", 16384, 3456, 1280, align=8).kernel == B.KERNEL_TILED   # A not 16-byte aligned
     assert B.plan("fwd", 16384, 3456, 1280, align=2).kernel == B.KERNEL_TILED   # A misaligned
     assert B.plan("fwd", 16384, 3456, 1296).kernel == B.KERNEL_TILED    # K % 64 != 0
     assert B.plan("fwd", 2048, 2048, 65536).kernel == B.KERNEL_TILED    # 60 tiles of 512 x 144
@@ -181,6 +187,8 @@ def test_kernel_choice():
     assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
     for s in STREAM_SHAPES:
         assert B.plan("fwd", *s).kernel == B.KERNEL_STREAM, s
+    for s in DBUF_SHAPES:
+        assert B.plan("fwd", *s).kernel == B.KERNEL_DBUF, s
     for s in SKINNY_SHAPES:
         assert B.plan("fwd", *s).kernel == B.KERNEL_SKINNY, s
     assert B.plan("fwd", 33, 16384, 16384).kernel != B.KERNEL_SKINNY   # more than 32 rows
@@ -266,8 +274,9 @@ def test_same_xcd_tiles_share_rows():
 
 def test_headline_plan():
     pl = B.plan("fwd", 16384, 3456, 1280)
-    assert (pl.tile_rows, pl.tile_cols) == (512, 144)
-    assert pl.tiles == 64 * 12 and pl.workgroups == 256 and pl.tiles_per_workgroup == 3
+    assert (pl.kernel, pl.tile_rows, pl.tile_cols) == (B.KERNEL_DBUF, 256, 96)
+    assert pl.tiles == 64 * 36 and pl.workgroups == 256 and pl.tiles_per_workgroup == 9
+    assert pl.threads_per_workgroup == 512 and pl.lds_bytes == 3 * 4 * 96 * 64   # three four-step stages
     assert pl.fast_path == 1
     assert B.plan("fwd", 16384, 3456, 1280, align=2).fast_path == 0
     assert B.plan("fwd", 300, 272, 96).fast_path == 1        # 96 % 16 == 0
@@ -452,3 +461,24 @@ def test_dx_ws_checks():
     assert g(dC, Wp, rs, 1.0, dX, B.OUT_F32, M, N, K, ws, -5, None) == B.ERR_DIM
     assert g(dC, Wp, rs, 1.0, dX, B.OUT_BF16, M, N, K, rs - 8, 64, None) == B.ERR_ALIAS
     assert g(dC, Wp, rs, 1.0, dX, B.OUT_BF16, M, N, K, dX + M * K * 2 - 4, 64, None) == B.ERR_ALIAS
+
+
+@pytest.mark.parametrize("cus,xcds", [(64, 4), (80, 8), (304, 8), (256, 1)])
+def test_plans_follow_the_machine(cus, xcds):
+    # on a machine with other CU / XCD counts the persistent kernels launch
+    # one workgroup per CU, the order still covers every tile once, and the
+    # tile counts that choose a kernel scale with the CUs
+    for op, shape in (("fwd", (16384, 3456, 1280)), ("fwd", (16300, 3450, 640)), ("dx", (16384, 3456, 1280)),
+                      ("fwd", (300, 272, 96)), ("dw", (1782, 3456, 1280))):
+        pl = _coverage(op, *shape, cus=cus, xcds=xcds)
+        assert pl.xcds == xcds
+        if pl.kernel in (B.KERNEL_STREAM, B.KERNEL_DBUF):
+            assert pl.workgroups == cus
+            assert pl.tiles_per_workgroup == -(-(-(-pl.tiles // xcds)) // (cus // xcds))
+    # four 256 x 96 tiles per CU: 2304 tiles take the double-buffered kernel up to 576 CUs
+    assert B.plan("fwd", 16384, 3456, 1280, cus=576, xcds=8).kernel == B.KERNEL_DBUF
+    assert B.plan("fwd", 16384, 3456, 1280, cus=584, xcds=8).kernel == B.KERNEL_STREAM
+    # the split dX kernel serves outputs of at most one 128 x 144 tile per CU
+    assert B.plan("dx", 1782, 3456, 1280, cus=64, xcds=8).kernel == B.KERNEL_TILED
+    with pytest.raises(B.TernaryGemmError):
+        B.plan("fwd", 300, 272, 96, cus=100, xcds=8)     # CUs not a multiple of the XCDs

@@ -14,8 +14,8 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
-from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
-                    STREAM_SHAPES)
+from shapes import (DBUF_SHAPES, DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES,
+                    SKINNY_SHAPES, STREAM_SHAPES)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -154,6 +154,19 @@ def tile_of(op, M, N, K):
     return pl.tile_rows, pl.tile_cols, pl.fast_path
 
 
+@pytest.mark.parametrize("M,N,K", DBUF_SHAPES)
+def test_fwd_dbuf_shapes(M, N, K):
+    # the double-buffered forward (on this device's CU and XCD counts),
+    # every element against the oracle
+    cus, xcds = B.machine()
+    pl = B.plan("fwd", M, N, K, cus=cus, xcds=xcds)
+    say(f"fwd dbuf {M}x{N}x{K} kernel={pl.kernel} tiles={pl.tiles} per_wg={pl.tiles_per_workgroup} "
+        f"cus={cus} xcds={xcds}")
+    assert pl.kernel == B.KERNEL_DBUF
+    A, Wp = synth.fwd_inputs(M + N + K, M, N, K, 3)
+    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd dbuf {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", FWD_SHAPES)
 def test_fwd_shapes(M, N, K):
     say(f"fwd {M}x{N}x{K} plan={tile_of('fwd', M, N, K)}")
@@ -248,7 +261,8 @@ def test_misaligned_bases(offset):
 
 
 @pytest.mark.parametrize("op,M,N,K", [("fwd", 300, 272, 96), ("fwd", 4100, 1900, 80),
-                                      ("fwd", 27, 4099, 2112), ("dx", 299, 100, 268),
+                                      ("fwd", 27, 4099, 2112), ("fwd", 8197, 3000, 1536),
+                                      ("dx", 299, 100, 268),
                                       ("dx", 27, 640, 1296),
                                       ("dw", 97, 271, 299)])
 def test_writes_exactly_the_output(op, M, N, K):
