@@ -258,12 +258,6 @@ const char *ternary_gemm_status_str(int status);
                                   512 x 160 (dX): one persistent 8-wave
                                   workgroup per CU, operands loaded straight
                                   into LDS                                    */
-#define TGEMM_KERNEL_DBUF 5    /* forward, int32 output, K % 256 == 0, K >= 1024,
-                                  16-byte aligned A, 4-byte aligned Wpacked
-                                  and C, 32-bit offsets, at least four
-                                  256 x 96 tiles per CU: one persistent 4-wave
-                                  workgroup per CU, each wave storing its
-                                  previous tile while it computes the next  */
 #define TGEMM_KERNEL_SKINNY 4  /* forward with M <= 32, K % 64 == 0, 16-byte
                                   aligned A and Wpacked; dX with M <= 32,
                                   N % 64 == 0, K % 16 == 0, 16-byte aligned dC

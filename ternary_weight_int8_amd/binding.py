@@ -54,7 +54,7 @@ class TgemmPlan(ctypes.Structure):
     ]
 
 
-KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM, KERNEL_SKINNY, KERNEL_DBUF = 0, 2, 3, 4, 5   # TgemmPlan.kernel
+KERNEL_TILED, KERNEL_SPLIT, KERNEL_STREAM, KERNEL_SKINNY = 0, 2, 3, 4   # TgemmPlan.kernel
 
 
 class TernaryGemmError(RuntimeError):

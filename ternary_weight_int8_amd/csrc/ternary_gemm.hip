@@ -2093,401 +2093,6 @@ __global__ __launch_bounds__(256) void skinny_dx_sum(const v4i *__restrict__ par
   }
 }
 
-// ---------------------------------------------------------------------------
-// Double-buffered forward kernel (tgemm_dbuf): C[M][N] = A x W for outputs
-// with enough 256 x 96 tiles for a persistent grid, K % 256 == 0 and
-// K >= 1024.
-//
-// At the "500m" shapes [P10425 "Throughput"] the int32 output is nine tenths
-// of the bytes the product moves, so the kernel keeps HBM writing while it
-// computes: each wave holds two accumulator sets, and while it accumulates
-// tile t in one it stores tile t - 1 from the other, three registers per
-// step over the first sixteen steps of tile t.
-//
-// A workgroup of 8 waves (two per SIMD) owns a 256 x 96 tile; wave w
-// computes rows 32 w .. 32 w + 31 and all 96 columns, as 1 x 3 fragments of
-// 32 x 32 (v_mfma_i32_32x32x32_i8).
-//   A: straight into registers, three steps ahead, by buffer loads of 16
-//      rows x 64 bytes (lane l: row l % 16, 16-byte chunk l / 16).  One
-//      v_permlane16_swap per dword pair of the fragment's two 16-row halves
-//      gives lane l row l % 32 with chunk u + 2 (l / 32), for sub-step u
-//      (the two 32-deep MFMAs of a 64-step).
-//   W: the packed codes of a stage (four steps, 1536 dwords: three per lane)
-//      are loaded three stages ahead and decoded once per tile load
-//      [P10425 "What this adds"], two stages ahead, one dword per lane in
-//      each of the stage's first three steps, into one of three LDS buffers
-//      shared by the eight waves: per step, column n holds 64 bytes with
-//      chunk c at slot c ^ ((n >> 2) & 3), so that the fragment reads (16
-//      columns per 16 lanes, one chunk) and the decode writes (4 columns x 4
-//      chunks per 16 lanes) touch all 64 banks once.  Fragments take the
-//      same chunk per lane as A's.  With three buffers a wave reads the next
-//      stage's fragments before the barrier that ends the current stage.
-//      Nothing in a step depends on the wave's index, so each step is one
-//      basic block and its MFMAs interleave with the rest.
-//   MFMA: A as the instruction's first operand (rows of C), W as its second
-//      (columns): register r of lane l holds C[8 (r / 4) + 4 (l / 32) + r %
-//      4][l % 32] of a fragment, so one dword store writes two 128-byte row
-//      segments.
-//   Edges: each tile reads A and W through buffer resources based at its
-//      first row / column and ending at the operand's end, so rows and
-//      columns past the output read zeros (code 0 is weight 0).  A store
-//      carries its whole offset in the range-checked voffset: rows past the
-//      output fall past the C resource's end, and lanes of columns past it
-//      add their offset to 2^31; nothing outside C is written.
-// The contraction is reduced serially in registers, in int32, exactly.
-// ---------------------------------------------------------------------------
-namespace db {
-constexpr int kWaves = 8, kNT = 64 * kWaves;
-constexpr int BM = 256, BN = 96, TM = 32;
-constexpr int JG = BN / 32;                           // 32-column fragments of a wave
-constexpr int SS = 4;                                 // steps (of 64) per stage
-constexpr int kStepB = BN * BK;                       // decoded bytes of one step
-constexpr int kStageB = SS * kStepB;
-constexpr int kBufs = 3;
-constexpr int kLds = kBufs * kStageB;
-constexpr int kDwStep = BN * (BK / 16);               // packed dwords of one step
-constexpr int kPw = SS * BN * (BK / 16) / kNT;       // packed dwords per thread per stage
-constexpr int D = 3;                                  // A prefetch distance (steps)
-constexpr int kRing = D + 1;
-constexpr int kItSteps = SS;                          // steps per loop iteration (one stage)
-constexpr int kSpreadIt = 4;                          // iterations carrying the previous tile's stores
-constexpr int kAcc = JG * 16;                         // accumulator registers of one set
-constexpr int kStSteps = kSpreadIt * kItSteps;        // steps that carry stores
-constexpr int kStPerStep = kAcc / kStSteps;
-constexpr int kMinStages = kSpreadIt;                 // stages per tile, at least
-constexpr int kRsrcFlags = 0x00020000;                // raw buffer resource, 32-bit data format
-static_assert(kRing == kItSteps, "A ring period = loop iteration");
-static_assert(kStPerStep * kStSteps == kAcc, "stores spread evenly");
-static_assert(kPw * kNT == SS * kDwStep && kPw == SS - 1, "packed dwords: one per lane in each of a stage's first steps");
-}  // namespace db
-
-typedef int32_t v16i __attribute__((ext_vector_type(16)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-
-struct DbArgs {
-  const int8_t *A;
-  const uint8_t *Wp;
-  int32_t *C;
-  int32_t M, N, K, kb;           // kb = K / 4, the packed row stride
-  int32_t tiles_c, tiles;
-  int32_t nsteps, nst;           // K / 64, K / 256
-  int32_t xcds;                  // workgroup b runs on XCD b % xcds
-};
-
-__device__ __forceinline__ Rsrc db_rsrc(const void *base, int64_t off, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base)) + off, 0,
-                                           (int32_t)(bytes > 0 ? bytes : 0), db::kRsrcFlags);
-}
-
-// the buffer resources of a tile's A rows and W columns (a tile that does
-// not exist gets empty resources: its loads read zeros from nowhere), and of
-// its C block
-__device__ __forceinline__ Rsrc db_rsrc_a(const DbArgs &a, int32_t pos, bool valid) {
-  const int32_t m0 = pos / a.tiles_c * db::BM;
-  return db_rsrc(a.A, (int64_t)m0 * a.K, valid ? (int64_t)(a.M - m0) * a.K : 0);
-}
-__device__ __forceinline__ Rsrc db_rsrc_w(const DbArgs &a, int32_t pos, bool valid) {
-  const int32_t n0 = pos % a.tiles_c * db::BN;
-  return db_rsrc(a.Wp, (int64_t)n0 * a.kb, valid ? (int64_t)(a.N - n0) * a.kb : 0);
-}
-__device__ __forceinline__ Rsrc db_rsrc_c(const DbArgs &a, int32_t pos) {
-  const int32_t m0 = pos / a.tiles_c * db::BM, n0 = pos % a.tiles_c * db::BN;
-  return db_rsrc(a.C, ((int64_t)m0 * a.N + n0) * 4, ((int64_t)(a.M - m0) * a.N - n0) * 4);
-}
-
-// Loads run ahead of the computation through two cursors: A's (a step: its
-// resource and byte offset) and W's (a stage).  Each moves on to the next
-// tile's resource at the end of the current tile's contraction.
-struct DbCursor {
-  Rsrc r;
-  int32_t off;
-};
-
-struct DbState {
-  // per lane
-  uint32_t voffA[2];             // A load h: row 32 w + 16 h + l % 16, chunk l / 16
-  uint32_t voffW[db::kPw];       // packed dword of a stage
-  uint32_t ldsWr[db::kPw];       // its decoded chunk in a stage buffer
-  uint32_t ldsRd[2];             // fragment read of sub-step u in a stage buffer
-  uint32_t sbase[db::JG];        // store offsets of the tile being stored (past 2^31: column past N)
-  // uniform
-  DbCursor ca, cw;               // next A step / W stage to load
-  Rsrc na, nw;                   // the next tile's A and W resources
-  Rsrc pc;                       // C resource of the tile being stored
-  int32_t G;                     // global stage counter of the current stage
-  int32_t wave;
-};
-
-struct DbRing {   // A loads in flight: [slot][half]
-  v4u x[db::kRing][2];
-};
-
-// issue the A loads of the cursor's step into ring slot SLOT, then advance
-template <int SLOT>
-__device__ __forceinline__ void db_load_a(DbRing &ring, DbState &st, const DbArgs &a) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    ring.x[SLOT][h] = __builtin_amdgcn_raw_buffer_load_b128(st.ca.r, st.voffA[h], st.ca.off, 0);
-  st.ca.off += BK;
-  if (st.ca.off == a.K) {
-    st.ca.off = 0;
-    st.ca.r = st.na;
-  }
-}
-
-// issue the packed W loads of the cursor's stage, then advance
-__device__ __forceinline__ void db_load_w(uint32_t (&pw)[db::kPw], DbState &st, const DbArgs &a) {
-#pragma unroll
-  for (int i = 0; i < db::kPw; ++i) pw[i] = __builtin_amdgcn_raw_buffer_load_b32(st.cw.r, st.voffW[i], st.cw.off, 0);
-  st.cw.off += db::SS * (BK / 4);
-  if (st.cw.off == a.kb) {
-    st.cw.off = 0;
-    st.cw.r = st.nw;
-  }
-}
-
-// register q of an accumulator set: fragment jg, register r, and the
-// fragment-local row of lanes 0..31 (lanes 32..63 hold row + 4)
-template <int Q>
-struct DbIdx {
-  static constexpr int jg = Q / 16, r = Q % 16;
-  static constexpr int row = 8 * (r / 4) + r % 4;
-};
-
-template <int Q>
-__device__ __forceinline__ void db_store1(const v16i (&accp)[db::JG], const DbState &st, int32_t N4) {
-  typedef DbIdx<Q> I;
-  const uint32_t voff = st.sbase[I::jg] + (uint32_t)(I::row * N4);
-  __builtin_amdgcn_raw_buffer_store_b32(accp[I::jg][I::r], st.pc, voff, 0, 0);
-}
-
-template <int Q, int E>
-__device__ __forceinline__ void db_stores(const v16i (&accp)[db::JG], const DbState &st, int32_t N4) {
-  if constexpr (E > 0) {
-    db_store1<Q>(accp, st, N4);
-    db_stores<Q + 1, E - 1>(accp, st, N4);
-  }
-}
-
-__device__ __forceinline__ void db_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// the packed dword i of this lane, decoded into stage buffer dst
-template <int I>
-__device__ __forceinline__ void db_decode(const uint32_t (&pw)[db::kPw], const DbState &st, int8_t *dst) {
-  *reinterpret_cast<v4i *>(dst + st.ldsWr[I]) = decode16(pw[I]);
-}
-
-// One step S of the tile (ring slot and step of the stage SLOT, fragments
-// wf[SLOT % 2]; S < 0: a step past the ones that carry stores): issues the
-// A loads D steps ahead, forms the step's A fragments, reads the W fragments
-// of the next step, runs the 6 MFMAs, decodes this lane's dword SLOT of the
-// packed codes of stage G + 2 and, with STORE, registers 3 S .. 3 S + 2 of
-// the previous tile.  FIRST: the tile's first step (accumulators start at
-// 0).  The instruction order inside a step is fixed by scheduling groups, so
-// that the MFMAs issue back to back with the other work in between.
-template <int SLOT, int S, bool FIRST, bool STORE>
-__device__ __forceinline__ void db_step(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
-                                        v4i (&wf)[2][db::JG][2], const uint32_t (&pw)[db::kPw], DbState &st,
-                                        const DbArgs &a, int8_t *smem) {
-  using namespace db;
-  constexpr int P = SLOT % 2;            // fragment set of this step
-  __builtin_amdgcn_sched_barrier(0);
-  db_load_a<(SLOT + D) % kRing>(ring, st, a);
-  v4i af[2];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const v2u p = __builtin_amdgcn_permlane16_swap(ring.x[SLOT][0][d], ring.x[SLOT][1][d], false, false);
-    af[0][d] = (int32_t)p[0];
-    af[1][d] = (int32_t)p[1];
-  }
-  {
-    // fragments of the next step: this stage's next step, or the next
-    // stage's first (decoded during the previous stage, published by its
-    // barrier)
-    constexpr bool last = SLOT == SS - 1;
-    const int32_t buf = (last ? st.G + 1 : st.G) % kBufs;
-    const int8_t *base = smem + buf * kStageB + (last ? 0 : (SLOT + 1) * kStepB);
-#pragma unroll
-    for (int jg = 0; jg < JG; ++jg)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        wf[1 - P][jg][u] = *reinterpret_cast<const v4i *>(base + st.ldsRd[u] + jg * 32 * BK);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int jg = 0; jg < JG; ++jg)
-      acc[jg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[u], wf[P][jg][u], (FIRST && u == 0) ? v16i{} : acc[jg],
-                                                      0, 0, 0);
-  if constexpr (SLOT < kPw) db_decode<SLOT>(pw, st, smem + ((st.G + 2) % kBufs) * kStageB);
-  if constexpr (STORE && S >= 0 && S < kStSteps) db_stores<S * kStPerStep, kStPerStep>(accp, st, 4 * a.N);
-  // order: the A loads, the swaps, then each MFMA followed by a share of the
-  // VALU work, an LDS access and a memory access
-  __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // A loads
-  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // swaps
-#pragma unroll
-  for (int k = 0; k < 2 * JG; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // VALU
-    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0); // LDS
-    __builtin_amdgcn_sched_group_barrier(0x040, 1, 0); // store
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// One stage (four steps), global stage st.G: pw[0] holds the packed codes
-// of stage G + 2 (decoded during this stage), pw[1] those of G + 3 (in
-// flight); at the end pw[1] moves to pw[0] and the stage after goes out.
-// IT < 0: an iteration past the ones that carry stores.
-template <bool FIRST, bool STORE, int IT>
-__device__ __forceinline__ void db_iter(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
-                                        v4i (&wf)[2][db::JG][2], uint32_t (&pw)[2][db::kPw], DbState &st,
-                                        const DbArgs &a, int8_t *smem) {
-  using namespace db;
-  constexpr int s0 = IT < 0 ? -100 : IT * kItSteps;
-  db_step<0, s0, FIRST, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
-  db_step<1, s0 + 1, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
-  db_step<2, s0 + 2, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
-  db_step<3, s0 + 3, false, STORE>(acc, accp, ring, wf, pw[0], st, a, smem);
-#pragma unroll
-  for (int i = 0; i < kPw; ++i) pw[0][i] = pw[1][i];
-  db_load_w(pw[1], st, a);
-  db_barrier();
-  st.G += 1;
-}
-
-// a whole tile: the first four iterations carry the previous tile's stores
-template <bool STORE>
-__device__ __forceinline__ void db_run_tile(v16i (&acc)[db::JG], const v16i (&accp)[db::JG], DbRing &ring,
-                                            v4i (&wf)[2][db::JG][2], uint32_t (&pw)[2][db::kPw], DbState &st,
-                                            const DbArgs &a, int8_t *smem) {
-  using namespace db;
-  static_assert(kSpreadIt == 4, "unrolled spread");
-  db_iter<true, STORE, 0>(acc, accp, ring, wf, pw, st, a, smem);
-  db_iter<false, STORE, 1>(acc, accp, ring, wf, pw, st, a, smem);
-  db_iter<false, STORE, 2>(acc, accp, ring, wf, pw, st, a, smem);
-  db_iter<false, STORE, 3>(acc, accp, ring, wf, pw, st, a, smem);
-  for (int32_t s0 = kSpreadIt * kItSteps; s0 < a.nsteps; s0 += kItSteps)
-    db_iter<false, false, -1>(acc, accp, ring, wf, pw, st, a, smem);
-}
-
-// the tile at position pos, just computed, becomes the one being stored;
-// the loads run on into the tile at pos_after (if there is one: has_after)
-__device__ __forceinline__ void db_advance(DbState &st, const DbArgs &a, int32_t lane, int32_t pos,
-                                           int32_t pos_after, bool has_after) {
-  using namespace db;
-  st.pc = db_rsrc_c(a, pos);
-  const int32_t n0 = pos % a.tiles_c * BN, h = lane >> 5, c = lane & 31;
-#pragma unroll
-  for (int jg = 0; jg < JG; ++jg) {
-    const int32_t col = 32 * jg + c;
-    st.sbase[jg] = n0 + col < a.N ? (uint32_t)(((TM * st.wave + 4 * h) * a.N + col) * 4)
-                                  : 0x80000000u + (uint32_t)(col * 4);
-  }
-  st.na = db_rsrc_a(a, pos_after, has_after);
-  st.nw = db_rsrc_w(a, pos_after, has_after);
-}
-
-__global__ __attribute__((amdgpu_flat_work_group_size(db::kNT, db::kNT), amdgpu_waves_per_eu(2, 2)))
-void tgemm_dbuf(DbArgs a) {
-  using namespace db;
-  __builtin_assume(a.nst >= kMinStages && a.nsteps == SS * a.nst && a.K == BK * a.nsteps && a.kb * 4 == a.K);
-  __shared__ __attribute__((aligned(1024))) int8_t smem[kLds];
-  const int32_t tid = threadIdx.x, lane = tid & 63;
-
-  // tiles of this workgroup: the row-major tile positions are split into one
-  // contiguous run per XCD; the nx workgroups of an XCD take every nx-th
-  // position of its run, so the tiles an XCD works on at one time share A
-  // rows (and all of W) in its L2
-  const int32_t xcds = a.xcds, nx = (int32_t)gridDim.x / xcds;
-  const int32_t xcd = (int32_t)blockIdx.x % xcds, j0 = (int32_t)blockIdx.x / xcds;
-  const int32_t qx = a.tiles / xcds, rx = a.tiles % xcds;
-  const int32_t start = xcd * qx + (xcd < rx ? xcd : rx) + j0;
-  const int32_t cnt = qx + (xcd < rx ? 1 : 0);
-  const int32_t ntile = cnt > j0 ? (cnt - j0 + nx - 1) / nx : 0;
-  if (ntile == 0) return;
-
-  DbState st;
-  st.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    st.voffA[h] = (uint32_t)((TM * st.wave + 16 * h + (lane & 15)) * a.K + 16 * (lane >> 4));
-#pragma unroll
-  for (int i = 0; i < kPw; ++i) {
-    const int32_t p = tid + kNT * i, sx = p / kDwStep, rem = p % kDwStep, n = rem >> 2, c = rem & 3;
-    st.voffW[i] = (uint32_t)(n * a.kb + 16 * sx + 4 * c);
-    st.ldsWr[i] = (uint32_t)(sx * kStepB + n * BK + 16 * (c ^ ((n >> 2) & 3)));
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int32_t n = lane & 31, c = u + 2 * (lane >> 5);
-    st.ldsRd[u] = (uint32_t)(n * BK + 16 * (c ^ ((n >> 2) & 3)));
-  }
-#pragma unroll
-  for (int jg = 0; jg < JG; ++jg) st.sbase[jg] = 0x80000000u;
-  st.ca.r = db_rsrc_a(a, start, true);
-  st.cw.r = db_rsrc_w(a, start, true);
-  st.ca.off = 0;
-  st.cw.off = 0;
-  st.na = db_rsrc_a(a, start + nx, ntile > 1);
-  st.nw = db_rsrc_w(a, start + nx, ntile > 1);
-  st.pc = db_rsrc_c(a, start);
-  st.G = 0;
-
-  // prologue: A steps 0 .. D - 1 in flight; stages 0 and 1 decoded into
-  // buffers 0 and 1; packed stages 2 and 3 in flight; fragments of step 0
-  DbRing ring;
-  v4i wf[2][JG][2];
-  uint32_t pw[2][kPw];
-  db_load_w(pw[0], st, a);
-  db_load_w(pw[1], st, a);
-  db_load_a<0>(ring, st, a);
-  db_load_a<1>(ring, st, a);
-  db_load_a<2>(ring, st, a);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    db_decode<0>(pw[b], st, smem + b * kStageB);
-    db_decode<1>(pw[b], st, smem + b * kStageB);
-    db_decode<2>(pw[b], st, smem + b * kStageB);
-  }
-  db_load_w(pw[0], st, a);
-  db_load_w(pw[1], st, a);
-  db_barrier();
-#pragma unroll
-  for (int jg = 0; jg < JG; ++jg)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) wf[0][jg][u] = *reinterpret_cast<const v4i *>(smem + st.ldsRd[u] + jg * 32 * BK);
-
-  v16i acc0[JG], acc1[JG];
-  db_run_tile<false>(acc0, acc1, ring, wf, pw, st, a, smem);
-  int32_t pos = start;
-  for (int32_t it = 1;; it += 2) {
-    if (it >= ntile) {
-      db_advance(st, a, lane, pos, pos, false);
-      db_stores<0, kAcc>(acc0, st, 4 * a.N);
-      break;
-    }
-    db_advance(st, a, lane, pos, pos + 2 * nx, it + 1 < ntile);
-    pos += nx;
-    db_run_tile<true>(acc1, acc0, ring, wf, pw, st, a, smem);
-    if (it + 1 >= ntile) {
-      db_advance(st, a, lane, pos, pos, false);
-      db_stores<0, kAcc>(acc1, st, 4 * a.N);
-      break;
-    }
-    db_advance(st, a, lane, pos, pos + 2 * nx, it + 2 < ntile);
-    pos += nx;
-    db_run_tile<true>(acc0, acc1, ring, wf, pw, st, a, smem);
-  }
-  // loads past the last tile (of empty resources) and the stores complete
-  // before the wave ends
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
 template <int OP, class T, bool FAST>
 hipError_t launch_t(const Args &a, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_kernel<OP, T, FAST>), dim3(a.tiles), dim3(kThreads), 0, stream, a);
@@ -2509,7 +2114,7 @@ hipError_t launch_f(const Args &a, bool fast, hipStream_t stream) {
 // (A variant that loads the int8 operand of the forward and dX straight into
 // MFMA registers, without LDS, measured no faster in the three-product step
 // on MI355X and was left out.)
-enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3, KSKINNY = 4, KDBUF = 5 };
+enum KernelId { KTILED = 0, KSPLIT = 2, KSTREAM = 3, KSKINNY = 4 };
 
 // The machine the plans are made for: compute units (one persistent
 // workgroup each) and XCDs (workgroup b runs on XCD b % xcds, each XCD with
@@ -2660,34 +2265,6 @@ void launch_skinny(const KArgs &ka, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((tgemm_skinny<MF, NB, AL>), dim3(grid), dim3(sk::kNT), 0, stream, ka);
 }
 
-// The double-buffered forward (tgemm_dbuf): int32 output, K % 256 == 0 and
-// K >= 1024 (whole four-step stages, at least the four stages that carry
-// the previous tile's stores), 16-byte aligned A, 4-byte aligned Wpacked and
-// C, 32-bit buffer offsets (C with its rows rounded up to whole tiles), and
-// at least four 256 x 96 tiles per CU, so that most of the stores overlap a
-// later tile's computation.
-struct DbPlan {
-  bool ok;
-  int32_t tiles_c, tiles, grid, xcds;
-};
-
-DbPlan dbuf_plan(int op, int kind, int64_t M, int64_t N, int64_t K, uintptr_t qalign, uintptr_t walign,
-                 uintptr_t oalign, const Machine &mc) {
-  DbPlan d{};
-  if (op != FWD || kind != OUT_I32 || !machine_ok(mc)) return d;
-  if (K % (db::SS * BK) != 0 || K / (db::SS * BK) < db::kMinStages) return d;
-  if (qalign % 16 != 0 || walign % 4 != 0 || oalign % 4 != 0) return d;
-  const int64_t tr = ceil_div(M, db::BM), tc = ceil_div(N, db::BN);
-  if (M > INT32_MAX / K || N > INT32_MAX / (K / 4) || tr * db::BM > INT32_MAX / (4 * N)) return d;
-  if (tr * tc < 4 * (int64_t)mc.cus || tr * tc > INT32_MAX) return d;
-  d.ok = true;
-  d.tiles_c = (int32_t)tc;
-  d.tiles = (int32_t)(tr * tc);
-  d.grid = mc.cus;
-  d.xcds = mc.xcds;
-  return d;
-}
-
 // the contraction split between two halves of a workgroup: dW on the
 // 128 x 144 tile, and dX on that tile when its tiles do not fill the CUs;
 // at least 8 steps
@@ -2784,26 +2361,6 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   a.xcds = mc.xcds;
   const bool fast = fast_ok(op, M, N, K, align_of(q), align_of(p));
 
-  {
-    const DbPlan d = dbuf_plan(op, kind, M, N, K, align_of(q), align_of(p), align_of(out), mc);
-    if (d.ok) {
-      DbArgs da;
-      da.A = q;
-      da.Wp = static_cast<const uint8_t *>(p);
-      da.C = static_cast<int32_t *>(out);
-      da.M = (int32_t)M;
-      da.N = (int32_t)N;
-      da.K = (int32_t)K;
-      da.kb = (int32_t)(K / 4);
-      da.tiles_c = d.tiles_c;
-      da.tiles = d.tiles;
-      da.nsteps = (int32_t)(K / BK);
-      da.nst = (int32_t)(K / (db::SS * BK));
-      da.xcds = d.xcds;
-      hipLaunchKernelGGL(tgemm_dbuf, dim3(d.grid), dim3(db::kNT), 0, stream, da);
-      return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
-    }
-  }
   {
     const SkinnyPlan kp = skinny_plan(op, M, N, K, align_of(q), align_of(p), mc);
     if (kp.ok) {
@@ -3028,21 +2585,6 @@ int ternary_gemm_plan_on(int op, int64_t M, int64_t N, int64_t K, int64_t align,
   plan->fast_path = fast_ok(op, M, N, K, al, al) ? 1 : 0;
   plan->xcds = mc.xcds;
   {
-    const DbPlan d = dbuf_plan(op, OUT_I32, M, N, K, al, al, al, mc);
-    if (d.ok) {
-      plan->tile_rows = db::BM;
-      plan->tile_cols = db::BN;
-      plan->tiles = d.tiles;
-      plan->workgroups = d.grid;
-      plan->tiles_per_workgroup = ceil_div(ceil_div(d.tiles, mc.xcds), d.grid / mc.xcds);
-      plan->band_cols = d.tiles_c;
-      plan->kernel = KDBUF;
-      plan->threads_per_workgroup = db::kNT;
-      plan->lds_bytes = db::kLds;
-      return TGEMM_OK;
-    }
-  }
-  {
     SkinnyPlan kp = skinny_plan(op, M, N, K, al, al, mc);
     if (!kp.ok) kp = skinny_dx_plan(op, M, N, K, al, al, mc);
     if (kp.ok) {
@@ -3101,7 +2643,7 @@ int ternary_gemm_tile_of(const tgemm_plan *plan, int64_t workgroup, int64_t iter
   const int32_t tiles_c = (int32_t)ceil_div(plan->out_cols, plan->tile_cols);
   const int32_t tiles = (int32_t)plan->tiles, xcds = plan->xcds;
   int32_t tr, tc;
-  if (plan->kernel == KSTREAM || plan->kernel == KDBUF) {
+  if (plan->kernel == KSTREAM) {
     // the kernels' own order: one contiguous run of row-major tile positions
     // per XCD; workgroup b (XCD b % xcds) takes every nx-th position of its
     // run, starting at b / xcds

@@ -37,16 +37,6 @@ TILES = ((256, 128), (128, 144), (64, 64))
 STREAM_SHAPES = [(16300, 3450, 640), (15000, 3460, 192), (4096, 4608, 64), (8192, 2304, 128),
                  (40000, 1000, 2112)]
 
-# Shapes for the double-buffered forward kernel (K % 256 == 0, K >= 1024, at
-# least four 256 x 96 tiles per CU): the timed shape; ragged M and N (a last
-# column tile with 90 of its 96 columns, a last row tile with 5 of its 256
-# rows, so that some waves have no row inside the output); K = 1024 (no
-# iteration past the eight stages that carry the previous tile's stores),
-# 1536, 2048 and 4096; exactly four tiles per CU; tile counts that leave
-# some workgroups an odd and others an even number of tiles.
-DBUF_SHAPES = [(16384, 3456, 1280), (16300, 3450, 1280), (16384, 1536, 1024), (12800, 2400, 2048),
-               (8197, 3000, 1536), (10496, 2400, 4096), (40000, 1000, 2048)]
-
 # Shapes for the streaming dX kernel (contraction N % 64 == 0, K % 16 == 0, at
 # least 256 tiles of 512 x 160): the timed shape, ragged M with a last column
 # tile of 16 or 144 of its 160 columns, and one or two contraction steps.

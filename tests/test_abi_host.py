@@ -11,7 +11,7 @@ import pytest
 
 from ternary_weight_int8_amd import binding as B
 from golden_io import read_kv
-from shapes import (DBUF_SHAPES, DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
+from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES, SKINNY_SHAPES,
                     SPLIT_DX_SHAPES, STREAM_SHAPES, TILES)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -121,12 +121,11 @@ def _coverage(op, M, N, K, cus=None, xcds=None):
     ("fwd", 4100, 900, 84), ("dw", 16384, 3456, 1280), ("dx", 16384, 3456, 1280), ("dx", 1782, 3456, 1280),
     ("dx", 1782, 3456, 1280), ("dx", 1, 1, 4), ("dw", 1782, 3456, 1280), ("dw", 5, 3, 7)]
     + [("fwd",) + s for s in STREAM_SHAPES] + [("dx",) + s for s in DX_STREAM_SHAPES]
-    + [("fwd",) + s for s in DBUF_SHAPES]
     + [("fwd",) + s for s in SKINNY_SHAPES] + [("dx",) + s for s in SKINNY_DX_SHAPES])
 def test_every_output_tile_covered_once(op, M, N, K):
     pl = _coverage(op, M, N, K)
     assert pl.lds_bytes <= 160 * 1024
-    if pl.kernel in (B.KERNEL_STREAM, B.KERNEL_DBUF):
+    if pl.kernel == B.KERNEL_STREAM:
         assert pl.threads_per_workgroup == 512
         assert pl.workgroups == 256 and pl.xcds == 8
         per_xcd = -(-pl.tiles // 8)
@@ -143,12 +142,12 @@ def test_parity_shapes_reach_every_tile_and_path():
     # the GPU parity shape lists exercise every tile shape on both load paths,
     # and every kernel on each load path it serves
     kernels = {"fwd": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1),
-                       (B.KERNEL_SKINNY, 1), (B.KERNEL_DBUF, 1)},
+                       (B.KERNEL_SKINNY, 1)},
                "dx": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_STREAM, 1), (B.KERNEL_SKINNY, 1),
                       (B.KERNEL_SPLIT, 0), (B.KERNEL_SPLIT, 1)},
                "dw": {(B.KERNEL_TILED, 0), (B.KERNEL_TILED, 1), (B.KERNEL_SPLIT, 0),
                       (B.KERNEL_SPLIT, 1)}}
-    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES + DBUF_SHAPES),
+    for op, shapes in (("fwd", FWD_SHAPES + STREAM_SHAPES + SKINNY_SHAPES),
                        ("dx", DX_SHAPES + DX_STREAM_SHAPES + SKINNY_DX_SHAPES),
                        ("dw", DW_SHAPES)):
         seen, seen_k = set(), set()
@@ -163,10 +162,10 @@ def test_parity_shapes_reach_every_tile_and_path():
 
 
 def test_kernel_choice():
-    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_DBUF
-    assert B.plan("fwd", 16384, 3456, 1408).kernel == B.KERNEL_STREAM   # K % 256 != 0
-    assert B.plan("fwd", 16384, 3456, 768).kernel == B.KERNEL_STREAM    # K < 1024
-    assert B.plan("fwd", 6144, 3456, 1280).kernel == B.KERNEL_STREAM    # 864 tiles of 256 x 96
+    assert B.plan("fwd", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
+    assert B.plan("fwd", 16384, 3456, 1408).kernel == B.KERNEL_STREAM
+    assert B.plan("fwd", 16384, 3454, 1280).kernel == B.KERNEL_STREAM   # N % 4 != 0: 4-byte stores
+    assert B.plan("fwd", 6144, 3456, 1280).kernel == B.KERNEL_STREAM    # 288 tiles of 512 x 144
     assert B.plan("fwd", 16384, 3456, 1280, align=8).kernel == B.KERNEL_TILED   # A not 16-byte aligned
     assert B.plan("fwd", 16384, 3456, 1280, align=2).kernel == B.KERNEL_TILED   # A misaligned
     assert B.plan("fwd", 16384, 3456, 1296).kernel == B.KERNEL_TILED    # K % 64 != 0
@@ -187,8 +186,6 @@ def test_kernel_choice():
     assert B.plan("fwd", 300, 272, 96).kernel == B.KERNEL_TILED
     for s in STREAM_SHAPES:
         assert B.plan("fwd", *s).kernel == B.KERNEL_STREAM, s
-    for s in DBUF_SHAPES:
-        assert B.plan("fwd", *s).kernel == B.KERNEL_DBUF, s
     for s in SKINNY_SHAPES:
         assert B.plan("fwd", *s).kernel == B.KERNEL_SKINNY, s
     assert B.plan("fwd", 33, 16384, 16384).kernel != B.KERNEL_SKINNY   # more than 32 rows
@@ -274,9 +271,9 @@ def test_same_xcd_tiles_share_rows():
 
 def test_headline_plan():
     pl = B.plan("fwd", 16384, 3456, 1280)
-    assert (pl.kernel, pl.tile_rows, pl.tile_cols) == (B.KERNEL_DBUF, 256, 96)
-    assert pl.tiles == 64 * 36 and pl.workgroups == 256 and pl.tiles_per_workgroup == 9
-    assert pl.threads_per_workgroup == 512 and pl.lds_bytes == 3 * 4 * 96 * 64   # three four-step stages
+    assert (pl.kernel, pl.tile_rows, pl.tile_cols) == (B.KERNEL_STREAM, 512, 144)
+    assert pl.tiles == 32 * 24 and pl.workgroups == 256 and pl.tiles_per_workgroup == 3
+    assert pl.threads_per_workgroup == 512 and pl.lds_bytes <= 160 * 1024
     assert pl.fast_path == 1
     assert B.plan("fwd", 16384, 3456, 1280, align=2).fast_path == 0
     assert B.plan("fwd", 300, 272, 96).fast_path == 1        # 96 % 16 == 0
@@ -472,12 +469,12 @@ def test_plans_follow_the_machine(cus, xcds):
                       ("fwd", (300, 272, 96)), ("dw", (1782, 3456, 1280))):
         pl = _coverage(op, *shape, cus=cus, xcds=xcds)
         assert pl.xcds == xcds
-        if pl.kernel in (B.KERNEL_STREAM, B.KERNEL_DBUF):
+        if pl.kernel == B.KERNEL_STREAM:
             assert pl.workgroups == cus
             assert pl.tiles_per_workgroup == -(-(-(-pl.tiles // xcds)) // (cus // xcds))
-    # four 256 x 96 tiles per CU: 2304 tiles take the double-buffered kernel up to 576 CUs
-    assert B.plan("fwd", 16384, 3456, 1280, cus=576, xcds=8).kernel == B.KERNEL_DBUF
-    assert B.plan("fwd", 16384, 3456, 1280, cus=584, xcds=8).kernel == B.KERNEL_STREAM
+    # at least one 512 x 144 tile per CU: 768 tiles take the stream kernel up to 768 CUs
+    assert B.plan("fwd", 16384, 3456, 1280, cus=768, xcds=8).kernel == B.KERNEL_STREAM
+    assert B.plan("fwd", 16384, 3456, 1280, cus=776, xcds=8).kernel == B.KERNEL_TILED
     # the split dX kernel serves outputs of at most one 128 x 144 tile per CU
     assert B.plan("dx", 1782, 3456, 1280, cus=64, xcds=8).kernel == B.KERNEL_TILED
     with pytest.raises(B.TernaryGemmError):

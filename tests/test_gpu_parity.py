@@ -14,7 +14,7 @@ import pytest
 import oracle
 from ternary_weight_int8_amd import binding as B
 from ternary_weight_int8_amd import synth
-from shapes import (DBUF_SHAPES, DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES,
+from shapes import (DW_SHAPES, DX_SHAPES, DX_STREAM_SHAPES, FWD_SHAPES, SKINNY_DX_SHAPES,
                     SKINNY_SHAPES, STREAM_SHAPES)
 
 torch = pytest.importorskip("torch")
@@ -152,19 +152,6 @@ def test_backward_pair(seed):
 def tile_of(op, M, N, K):
     pl = B.plan(op, M, N, K)
     return pl.tile_rows, pl.tile_cols, pl.fast_path
-
-
-@pytest.mark.parametrize("M,N,K", DBUF_SHAPES)
-def test_fwd_dbuf_shapes(M, N, K):
-    # the double-buffered forward (on this device's CU and XCD counts),
-    # every element against the oracle
-    cus, xcds = B.machine()
-    pl = B.plan("fwd", M, N, K, cus=cus, xcds=xcds)
-    say(f"fwd dbuf {M}x{N}x{K} kernel={pl.kernel} tiles={pl.tiles} per_wg={pl.tiles_per_workgroup} "
-        f"cus={cus} xcds={xcds}")
-    assert pl.kernel == B.KERNEL_DBUF
-    A, Wp = synth.fwd_inputs(M + N + K, M, N, K, 3)
-    assert_exact(gpu_fwd(A, Wp), oracle.fwd(A, Wp), f"fwd dbuf {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", FWD_SHAPES)
