@@ -59,10 +59,12 @@ typedef enum tgemm_status {
     TGEMM_ERR_BOUND = -4,  /* the contraction is longer than the exact-int32 bound */
     TGEMM_ERR_ALIAS = -5,  /* the output overlaps an input                       */
     TGEMM_ERR_HIP = -6,    /* the HIP runtime reported an error at launch        */
-    TGEMM_ERR_KIND = -7    /* the output kind of a scaled call is not one of
+    TGEMM_ERR_KIND = -7,   /* the output kind of a scaled call is not one of
                               TGEMM_OUT_F32, TGEMM_OUT_BF16, or the input kind
                               of a quantizer call not TGEMM_IN_F32,
                               TGEMM_IN_BF16                                   */
+    TGEMM_ERR_SCRATCH = -8 /* ternary_gemm_s8_dx_noalloc: the split needs more
+                              than TGEMM_STATIC_SCRATCH_BYTES of scratch      */
 } tgemm_status;
 
 /* Longest contraction for which every int32 result is exact whatever the
@@ -172,6 +174,26 @@ int ternary_gemm_s8_dx_scaled_ws(const int8_t *dC, const uint8_t *Wpacked, const
                                  float w_scale, void *dX, int out_kind,
                                  int64_t M, int64_t N, int64_t K, void *workspace,
                                  int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dX that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same product, arguments, checks and results as
+ * ternary_gemm_s8_dx_ws, with the workspace taken from a static device
+ * buffer of TGEMM_STATIC_SCRATCH_BYTES that the library holds on each device
+ * it runs on until the process ends (its address is looked up once per
+ * device, on the device's first call).  When the contraction split applies
+ * and needs more than that buffer (ternary_gemm_dx_workspace() bytes), the
+ * call returns TGEMM_ERR_SCRATCH and launches nothing; without a split it
+ * runs the one-pass kernels.  The call itself allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  Every call on a device
+ * shares that device's buffer, whose contents on entry do not matter: calls
+ * that may overlap on one device (two streams, two threads) race on it and
+ * must be serialized by the caller.
+ */
+#define TGEMM_STATIC_SCRATCH_BYTES (8 << 20)
+int ternary_gemm_s8_dx_noalloc(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX,
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* Workspace bytes the dX calls above use for these dimensions when the
  * inputs' base alignment is `align` bytes (the smallest power-of-two

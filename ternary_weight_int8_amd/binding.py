@@ -12,7 +12,8 @@ import os
 from .build import LIB
 
 OK = 0
-ERR_NULL, ERR_DIM, ERR_PACK, ERR_BOUND, ERR_ALIAS, ERR_HIP, ERR_KIND = -1, -2, -3, -4, -5, -6, -7
+ERR_NULL, ERR_DIM, ERR_PACK, ERR_BOUND, ERR_ALIAS, ERR_HIP, ERR_KIND, ERR_SCRATCH = -1, -2, -3, -4, -5, -6, -7, -8
+STATIC_SCRATCH_BYTES = 8 << 20   # TGEMM_STATIC_SCRATCH_BYTES
 OUT_F32, OUT_BF16 = 1, 2   # output kinds of the scaled calls
 IN_F32, IN_BF16 = 1, 2     # input kinds of the quantizer calls
 
@@ -35,6 +36,7 @@ EXPORTS = (
     "ternary_gemm_s8_dx_ws",
     "ternary_gemm_s8_dx_scaled_ws",
     "ternary_gemm_dx_workspace",
+    "ternary_gemm_s8_dx_noalloc",
 )
 
 OPS = {"fwd": 0, "dx": 1, "dw": 2}
@@ -108,6 +110,8 @@ def lib():
         L.ternary_gemm_s8_dx_ws.restype = ctypes.c_int
         L.ternary_gemm_s8_dx_scaled_ws.argtypes = [p, p, p, f32, p, i32, i64, i64, i64, p, i64, p]
         L.ternary_gemm_s8_dx_scaled_ws.restype = ctypes.c_int
+        L.ternary_gemm_s8_dx_noalloc.argtypes = [p, p, p, i64, i64, i64, p]
+        L.ternary_gemm_s8_dx_noalloc.restype = ctypes.c_int
         L.ternary_gemm_dx_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
         L.ternary_gemm_dx_workspace.restype = ctypes.c_int
         _lib = L
@@ -282,6 +286,24 @@ def ternary_gemm_s8_dx_ws(dC, Wpacked, K, workspace=None, dX=None, stream=None):
                                      _stream(stream, dX.device))
     if st != OK:
         raise TernaryGemmError("ternary_gemm_s8_dx_ws", st, status_str(st))
+    return dX
+
+
+def ternary_gemm_s8_dx_noalloc(dC, Wpacked, K, dX=None, stream=None):
+    """ternary_gemm_s8_dx with the library's static device scratch in place of
+    a workspace (the C call allocates nothing; dX is allocated here when not
+    given)."""
+    torch = _torch()
+    _check(dC, torch.int8, 2, "dC")
+    _check(Wpacked, torch.uint8, 2, "Wpacked")
+    M, N = dC.shape
+    if tuple(Wpacked.shape) != (N, K // 4) or K % 4:
+        raise ValueError(f"Wpacked must be [N][K/4] = [{N}][{K // 4}], got {tuple(Wpacked.shape)}")
+    dX = _output(dX, (M, K), torch.int32, dC.device, "dX")
+    st = lib().ternary_gemm_s8_dx_noalloc(dC.data_ptr(), Wpacked.data_ptr(), dX.data_ptr(), M, N, K,
+                                          _stream(stream, dX.device))
+    if st != OK:
+        raise TernaryGemmError("ternary_gemm_s8_dx_noalloc", st, status_str(st))
     return dX
 
 

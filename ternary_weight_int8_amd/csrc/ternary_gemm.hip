@@ -2469,6 +2469,30 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
 
+// Static scratch of ternary_gemm_s8_dx_noalloc: the split dX's partial sums
+// for callers that cannot allocate.  Each device holds its own copy from the
+// library's load until the process ends.  Host code never uses this name as
+// an address: scratch_of() looks the device address up once per device.
+constexpr int64_t kScratchBytes = TGEMM_STATIC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 16-byte vectors");
+static __device__ __align__(256) int32_t scratch[kScratchBytes / 4];
+
+// the current device's address of `scratch` (hipGetSymbolAddress with the
+// device current, once per device)
+int scratch_of(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TGEMM_ERR_HIP;
+  constexpr int kMaxDev = 64;
+  static std::atomic<void *> cache[kMaxDev];
+  void *ptr = dev < kMaxDev ? cache[dev].load(std::memory_order_acquire) : nullptr;
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TGEMM_ERR_HIP;
+    if (dev < kMaxDev) cache[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return TGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2527,6 +2551,22 @@ int ternary_gemm_s8_dx_ws(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX,
   return run(DX, dC, Wpacked, dX, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream, workspace, workspace_bytes);
 }
 
+int ternary_gemm_s8_dx_noalloc(const int8_t *dC, const uint8_t *Wpacked, int32_t *dX, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream) {
+  if (!dC || !Wpacked || !dX) return TGEMM_ERR_NULL;
+  const int st = check_dims(DX, M, N, K);
+  if (st != TGEMM_OK) return st;
+  Machine mc;
+  if (query_machine(&mc) != TGEMM_OK) return TGEMM_ERR_HIP;
+  const SplitDxPlan xp = skinny_dx_split_plan(DX, M, N, K, align_of(dC), align_of(Wpacked), mc);
+  if (!xp.ok) return run(DX, dC, Wpacked, dX, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream);
+  if (xp.bytes > kScratchBytes) return TGEMM_ERR_SCRATCH;
+  void *ws = nullptr;
+  const int sst = scratch_of(&ws);
+  if (sst != TGEMM_OK) return sst;
+  return run(DX, dC, Wpacked, dX, OUT_I32, nullptr, nullptr, 0.f, M, N, K, stream, ws, kScratchBytes);
+}
+
 int ternary_gemm_s8_dx_scaled_ws(const int8_t *dC, const uint8_t *Wpacked, const float *dc_row_scale,
                                  float w_scale, void *dX, int out_kind, int64_t M, int64_t N, int64_t K,
                                  void *workspace, int64_t workspace_bytes, hipStream_t stream) {
@@ -2555,6 +2595,7 @@ const char *ternary_gemm_status_str(int status) {
     case TGEMM_ERR_ALIAS: return "the output overlaps an input";
     case TGEMM_ERR_HIP: return "the HIP runtime reported an error at launch";
     case TGEMM_ERR_KIND: return "the output kind is not TGEMM_OUT_F32 or TGEMM_OUT_BF16";
+    case TGEMM_ERR_SCRATCH: return "the split needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

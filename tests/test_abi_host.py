@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in (B.OK, B.ERR_NULL, B.ERR_DIM, B.ERR_PACK, B.ERR_BOUND, B.ERR_ALIAS, B.ERR_HIP, B.ERR_KIND):
+    for st in (B.OK, B.ERR_NULL, B.ERR_DIM, B.ERR_PACK, B.ERR_BOUND, B.ERR_ALIAS, B.ERR_HIP, B.ERR_KIND,
+               B.ERR_SCRATCH):
         s = B.status_str(st)
         assert s and s != "unknown status"
     assert B.status_str(12345) == "unknown status"
@@ -479,3 +480,15 @@ def test_plans_follow_the_machine(cus, xcds):
     assert B.plan("dx", 1782, 3456, 1280, cus=64, xcds=8).kernel == B.KERNEL_TILED
     with pytest.raises(B.TernaryGemmError):
         B.plan("fwd", 300, 272, 96, cus=100, xcds=8)     # CUs not a multiple of the XCDs
+
+
+def test_noalloc_argument_checks_before_any_device_call():
+    # pointer and dimension errors return before the call touches a device
+    f = B.lib().ternary_gemm_s8_dx_noalloc
+    x = 1 << 20
+    assert f(None, x, x, 4, 4, 4, None) == B.ERR_NULL
+    assert f(x, None, x, 4, 4, 4, None) == B.ERR_NULL
+    assert f(x, x, None, 4, 4, 4, None) == B.ERR_NULL
+    assert f(x, x, x, 0, 4, 4, None) == B.ERR_DIM
+    assert f(x, x, x, 4, 4, 6, None) == B.ERR_PACK
+    assert "scratch" in B.status_str(B.ERR_SCRATCH)
