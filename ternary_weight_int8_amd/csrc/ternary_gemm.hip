@@ -45,10 +45,18 @@
 // Exactness: every partial sum is bounded by the final bound the host checks
 // (L * 128 for ternary, L * 128^2 for int8 x int8), so int32 accumulation in
 // any order is exact [P10425 "What this adds", "i32 overflow bound"; P10855
-// PR body, "k <= 131071"].  Each output is reduced inside one workgroup, in a
-// fixed order (dW at long contractions in two interleaved halves that are
-// added at the end): no split across workgroups, no atomics, identical bits
-// on every call.
+// PR body, "k <= 131071"], and every reduction order below gives the same
+// bits on every call, with no atomics.  Most kernels reduce each output
+// serially in one wave's registers.  Three split the contraction, each into
+// a fixed number of parts added in a fixed order:
+//   - tgemm_split (dW at long contractions, dX with few tiles): two halves of
+//     one workgroup take alternate steps; half 1 hands its sums to half 0
+//     through LDS;
+//   - the skinny kernels (M <= 32): the eight waves of a workgroup take
+//     interleaved steps and add their sums through LDS in wave order;
+//   - the workspace dX calls (ternary_gemm_s8_dx_ws, _scaled_ws, _noalloc):
+//     S workgroups take contiguous runs of the contraction and write int32
+//     partial sums; a second kernel adds them in split order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
