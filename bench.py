@@ -253,6 +253,52 @@ def skinny_rows(B, synth, torch, stream, seed, steps, op):
     return out
 
 
+def floors(B, torch, stream, M, N, steps):
+    """The bounds the forward's time is compared with, measured by the probe
+    library (csrc/roofline.hip) with HIP events on `stream`: a write-only
+    pass over an int32 buffer of the forward's output size (M x N), and
+    MFMA-only loops of each int8 shape, 8 waves per CU."""
+    import ctypes
+    from ternary_weight_int8_amd import build as hb
+    if not os.path.exists(hb.PROBE_LIB):
+        raise RuntimeError(f"{hb.PROBE_LIB} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(hb.PROBE_LIB)
+    L.tgemm_roofline_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    L.tgemm_roofline_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
+    cus, _ = B.machine()
+    s = stream.cuda_stream
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3   # seconds per launch
+
+    out = {}
+    buf = torch.empty(M * N, dtype=torch.int32, device=stream.device)
+    t = timed(lambda: L.tgemm_roofline_fill(buf.data_ptr(), M * N, 1, s), steps)
+    out["store_floor"] = {"bytes": M * N * 4, "us": t * 1e6, "tbs": M * N * 4 / t / 1e12,
+                          "note": "one write-only pass over the forward's int32 output size"}
+    del buf
+    mo = torch.empty(cus * 512, dtype=torch.int32, device=stream.device)
+    macs = ctypes.c_int64(0)
+    for shape, iters in ((16, 8000), (32, 4000)):
+        t = timed(lambda: L.tgemm_roofline_mfma(mo.data_ptr(), shape, iters, cus, ctypes.byref(macs), s),
+                  max(steps // 2, 1))
+        ops = 2 * macs.value
+        out[f"mfma_{shape}"] = {"tops": ops / t / 1e12, "frac": ops / t / PEAK_INT8_OPS,
+                                "instruction": {16: "v_mfma_i32_16x16x64_i8",
+                                                32: "v_mfma_i32_32x32x32_i8"}[shape],
+                                "note": "MFMAs only, independent accumulators, 2 waves per SIMD"}
+    return out
+
+
 def backward_rows(B, synth, torch, stream, seed, steps):
     """dX and dW of the pages' backward batch (1782 rows, N = 3456, K = 1280),
     warm inputs, each over `steps` launches, eagerly and replayed from one
@@ -381,6 +427,9 @@ def main():
     ap.add_argument("--prep-steps", type=int, default=50,
                     help="after the timed step, time the packer and the quantizers over this many "
                          "launches each (0: skip)")
+    ap.add_argument("--floor-steps", type=int, default=10,
+                    help="after the timed step, measure the store floor for the forward's output size "
+                         "and the MFMA-only rate with the probe kernels, over this many launches (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -524,6 +573,8 @@ def main():
         line["backward_1782"] = backward_rows(B, synth, torch, stream, args.seed, args.backward_steps)
     if args.prep_steps > 0 and not args.only:
         line["prep"] = prep_steps(B, synth, torch, stream, args.seed, args.prep_steps)
+    if args.floor_steps > 0 and not args.only:
+        line["floors"] = floors(B, torch, stream, M, N, args.floor_steps)
     if args.cpu_rows > 0 and int(os.environ.get("RANK", "0")) == 0:
         line["cpu_baseline"] = cpu_baseline(A, Wp, dC, K, min(args.cpu_rows, M))
     else:
