@@ -19,18 +19,31 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# TERNARY_ORACLE_LIB names another build of oracle.c to load instead (the
+# sanitizer test's; it is never built here)
+_LIB = os.environ.get("TERNARY_ORACLE_LIB") or _DEFAULT_LIB
 
-BUILD_CMD = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", _SRC, "-o", _LIB]
+BUILD_CMD = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", _SRC, "-o", _DEFAULT_LIB]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
 
 def build() -> str:
     """Compile liboracle.so (always; callers decide when)."""
-    tmp = _LIB + ".tmp"
+    tmp = _DEFAULT_LIB + ".tmp"
     cmd = BUILD_CMD[:-1] + [tmp]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, _DEFAULT_LIB)
+    return _DEFAULT_LIB
+
+
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code only) into `path`."""
+    subprocess.run(["gcc", *SANITIZE_FLAGS, "-std=c99", "-fPIC", "-shared", "-pthread", _SRC, "-o", path],
+                   check=True)
+    return path
 
 
 _lib = None
@@ -40,6 +53,8 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
+            if _LIB != _DEFAULT_LIB:
+                raise RuntimeError(f"TERNARY_ORACLE_LIB={_LIB} does not exist")
             build()
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
