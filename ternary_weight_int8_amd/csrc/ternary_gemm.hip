@@ -928,7 +928,23 @@ Shape shape_of(int op, int64_t M, int64_t N, int64_t K) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Pick the tile with the least estimated time: rounds of one workgroup per
-// CU times the MACs of one tile at that tile's efficiency.
+// CU times the MACs of one tile at that tile's efficiency.  dX of at least
+// 512 rows is the exception: when its 128 x 144 tiles would leave more than
+// half the CUs idle even with the contraction split inside each workgroup,
+// and its 64 x 64 tiles fill every CU, the small tiles win (several small
+// workgroups share a CU).  Measured on MI355X, dX at 1782 x 3456 x 1280 takes 24 against
+// 27.5 us, at 640 x 8192 x 2048 36 against 66 us; at 3000 x 3456 x 1280 (216
+// tiles of 128 x 144) the split tile stays faster, 30 against 34 us.
+int pick_tile(const Shape &s, int64_t cus);
+int pick_tile_for(int op, const Shape &s, int64_t cus) {
+  const int t = pick_tile(s, cus);
+  if (op != DX || t != TW) return t;
+  const TileInfo &w = kTileInfo[TW], &sm = kTileInfo[TS];
+  const int64_t tw = ceil_div(s.R, w.bm) * ceil_div(s.Cc, w.bn);
+  const int64_t ts = ceil_div(s.R, sm.bm) * ceil_div(s.Cc, sm.bn);
+  return s.R >= 4 * w.bm && 2 * tw <= cus && ts >= cus ? TS : t;
+}
+
 int pick_tile(const Shape &s, int64_t cus) {
   int best = TS;
   double best_cost = 0;
@@ -2352,7 +2368,7 @@ int run(int op, const int8_t *q, const void *p, void *out, int kind, const float
   o.vec = (s.Cc % 4 == 0 && aligned(out, 4 * esz)) ? 1 : 0;
   o.vec8 = (kind == OUT_BF16 && s.Cc % 8 == 0 && aligned(out, 16)) ? 1 : 0;
 
-  const int tile = pick_tile(s, mc.cus);
+  const int tile = pick_tile_for(op, s, mc.cus);
   const TileInfo &ti = kTileInfo[tile];
   Args a;
   a.q = q;
@@ -2664,7 +2680,7 @@ int ternary_gemm_plan_on(int op, int64_t M, int64_t N, int64_t K, int64_t align,
       return TGEMM_OK;
     }
   }
-  const int tile = pick_tile(s, mc.cus);
+  const int tile = pick_tile_for(op, s, mc.cus);
   const TileInfo &ti = kTileInfo[tile];
   plan->tile_rows = ti.bm;
   plan->tile_cols = ti.bn;

@@ -15,10 +15,14 @@ DX_SHAPES = [  # contraction N; the fast path needs N % 16 == K % 16 == 0
     (4100, 80, 3904), (4100, 84, 3900),
     (300, 96, 272), (299, 100, 268),
     (1, 1, 4), (1, 16, 16), (27, 3456, 1280), (1, 4, 4100),
-    # 128 x 144 tiles too few to fill the CUs: the contraction split between
-    # two halves of a workgroup; the pages' backward batch, a ragged last
-    # step, odd step counts on the byte path, a long contraction
-    (1782, 3456, 1280), (1782, 3440, 1296), (1500, 1030, 1152), (1300, 900, 1436), (640, 8192, 2048)]
+    # 128 x 144 tiles leaving more than half the CUs idle: 64 x 64 tiles; the
+    # pages' backward batch, a ragged last step, odd step counts on the byte
+    # path, a long contraction
+    (1782, 3456, 1280), (1782, 3440, 1296), (1500, 1030, 1152), (1300, 900, 1436), (640, 8192, 2048),
+    # 128 x 144 tiles filling more than half of the CUs but not all of them:
+    # the contraction split between two halves of a workgroup, on the vector
+    # and the byte path
+    (3000, 3456, 1280), (2600, 3450, 1284)]
 
 DW_SHAPES = [  # contraction M; the fast path needs N % 16 == K % 16 == 0
     (80, 3904, 8208), (81, 3901, 8201),

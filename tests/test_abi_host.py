@@ -174,9 +174,12 @@ def test_kernel_choice():
     assert B.plan("dx", 16384, 3456, 1280).kernel == B.KERNEL_STREAM
     assert B.plan("dx", 16384, 3456, 1288).kernel == B.KERNEL_TILED    # K % 16 != 0
     assert B.plan("dx", 16384, 3400, 1280).kernel == B.KERNEL_TILED    # N % 64 != 0
-    # 32 tiles of 512 x 160 are too few for the stream kernel; 126 of 128 x 144
-    # take the contraction split between two halves of a workgroup
+    # 32 tiles of 512 x 160 are too few for the stream kernel, and 126 of
+    # 128 x 144 would leave half the CUs idle: 560 tiles of 64 x 64; 216 tiles
+    # of 128 x 144 take the contraction split between two halves of a workgroup
     pl = B.plan("dx", 1782, 3456, 1280)
+    assert (pl.kernel, pl.tile_rows, pl.tile_cols, pl.threads_per_workgroup) == (B.KERNEL_TILED, 64, 64, 256)
+    pl = B.plan("dx", 3000, 3456, 1280)
     assert (pl.kernel, pl.tile_rows, pl.tile_cols, pl.threads_per_workgroup) == (B.KERNEL_SPLIT, 128, 144, 512)
     assert B.plan("dx", 4100, 80, 3904).kernel == B.KERNEL_TILED     # 924 tiles fill the CUs
     assert B.plan("dx", 4100, 80, 912).kernel == B.KERNEL_TILED      # 2 steps
