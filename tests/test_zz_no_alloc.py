@@ -90,3 +90,34 @@ def test_noalloc_rejects_a_split_past_the_static_buffer():
     assert bool((out == -7).all())     # nothing launched
     with pytest.raises(B.TernaryGemmError):
         B.ternary_gemm_s8_dx_noalloc(dC, Wp, K)
+
+
+def test_noalloc_inside_a_captured_graph():
+    # the callers it is for: code under graph capture.  Captured once after an
+    # eager call, replayed three times with eager work between the replays,
+    # every replay equal to the eager result
+    M, N, K = 27, 8192, 8192
+    dC, Wp = _inputs(11, M, N, K)
+    out = torch.empty((M, K), dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.ternary_gemm_s8_dx_noalloc(dC, Wp, K, dX=out, stream=side)
+    side.synchronize()
+    eager = out.clone()
+    ref, nbytes = _with_workspace(dC, Wp, M, N, K)
+    assert nbytes > 0 and torch.equal(eager, ref)
+    say(f"noalloc dX in a graph {M}x{N}x{K}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        B.ternary_gemm_s8_dx_noalloc(dC, Wp, K, dX=out, stream=side)
+    other = _inputs(12, 5, 4096, 8192)
+    for rep in range(3):
+        out.zero_()
+        # eager no-alloc work between the replays, on the same static scratch
+        junk = torch.empty((5, 8192), dtype=torch.int32, device=DEV)
+        assert _noalloc(*other, junk, 5, 4096, 8192) == B.OK
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager result"
