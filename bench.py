@@ -437,7 +437,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+              "(each GPU would run these kernels on its own shard of the batch).", file=sys.stderr)
         sys.exit(2)
 
     import torch
